@@ -1,0 +1,51 @@
+"""Brute-force attention in pure Python (no numpy, no BLAS) for tiny grids.
+
+TEST INFRASTRUCTURE ONLY (see oracle/attention.py).  Written independently of
+oracle/attention.py, straight from the definition, one scalar at a time, so the
+vectorised oracle can be checked against it.
+"""
+from __future__ import annotations
+
+import math
+
+
+def _normalise_rotate(vec, weight, t, h, w, theta, eps):
+    d = len(vec)
+    ms = sum(x * x for x in vec) / d
+    inv = 1.0 / math.sqrt(ms + eps)
+    xn = [vec[c] * weight[c] * inv for c in range(d)]
+    out = list(xn)
+    for axis, pos in enumerate((t, h, w)):
+        for i in range(16):
+            e = 32 * axis + 2 * i
+            ang = pos * theta ** (-(2.0 * i) / 32.0)
+            co, si = math.cos(ang), math.sin(ang)
+            out[e] = xn[e] * co - xn[e + 1] * si
+            out[e + 1] = xn[e] * si + xn[e + 1] * co
+    return out
+
+
+def attention(Q, K, V, wq, wk, T, H, W, theta=1e4, eps=1e-6, mask=None, block=128):
+    """O[n][head][c] as nested lists; Q/K/V given as nested [N][heads][96] sequences."""
+    N = T * H * W
+    heads = len(Q[0])
+    d = len(Q[0][0])
+    wq = [float(x) for x in wq]
+    wk = [float(x) for x in wk]
+    pos = [((n // (H * W)), (n // W) % H, n % W) for n in range(N)]
+    out = [[[0.0] * d for _ in range(heads)] for _ in range(N)]
+    for hd in range(heads):
+        qs = [_normalise_rotate([float(x) for x in Q[n][hd]], wq, *pos[n], theta, eps) for n in range(N)]
+        ks = [_normalise_rotate([float(x) for x in K[n][hd]], wk, *pos[n], theta, eps) for n in range(N)]
+        for i in range(N):
+            keys = [j for j in range(N)
+                    if mask is None or mask[hd][i // block][j // block]]
+            if not keys:
+                continue
+            lg = [sum(qs[i][c] * ks[j][c] for c in range(d)) / math.sqrt(d) for j in keys]
+            top = max(lg)
+            ex = [math.exp(x - top) for x in lg]
+            tot = sum(ex)
+            for c in range(d):
+                out[i][hd][c] = sum(ex[a] * float(V[j][hd][c]) for a, j in enumerate(keys)) / tot
+    return out

@@ -1,0 +1,6 @@
+"""Seeded synthetic input generation shared by the tests, the bench and the oracle checks."""
+from .gen import (HEAD_DIM, WORKLOADS, BF16Tensor, Inputs, Workload, bf16_bits_to_f32,
+                  custom_workload, f32_to_bf16_bits, make_inputs)
+
+__all__ = ["HEAD_DIM", "WORKLOADS", "BF16Tensor", "Inputs", "Workload", "bf16_bits_to_f32",
+           "custom_workload", "f32_to_bf16_bits", "make_inputs"]
