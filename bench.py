@@ -1,0 +1,228 @@
+"""Benchmark of the DiT self-attention hot path on one MI355X.
+
+A step is one full layer: dense attention over the whole token grid for all heads
+(or, for a block-sparse workload, route + block-sparse attention).  Inputs are
+seeded synthetic bf16 tensors already resident in HBM when the timed region
+starts.  Prints ONE JSON line.
+
+    python bench.py [--steps K] [--warmup W] [--workload v5|image|v5s|v10s|v10d|...]
+                    [--no-cpu-baseline] [--calib-copy]
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "ms/layer + TFLOP/s (frac of bf16 MFMA peak), 124,992 tokens, 56 heads d=96"
+PEAK_BF16_TFLOPS = 2516.6    # MI355X dense bf16 MFMA: 256 CUs x 2.4 GHz x 4096 FLOP/clk/CU
+PEAK_HBM_GBS = 8000.0
+DESCR = {
+    "v5": "dense attention, 5 s 1344x768 video token grid 31x48x84 = 124,992 tokens, 56 heads x 96",
+    "image": "dense attention, image token grid 1x256x256 = 65,536 tokens, 56 heads x 96",
+    "v5s": "route + block-sparse attention (sparsity 0.75, 128-token blocks), 124,992 tokens, 56 heads x 96",
+    "v10s": "route + block-sparse attention (sparsity 0.80, 128-token blocks), 245,952 tokens, 56 heads x 96",
+    "v10d": "dense attention, 10 s video token grid 61x48x84 = 245,952 tokens, 56 heads x 96",
+}
+
+
+def log(msg):
+    print(msg, file=sys.stderr, flush=True)
+
+
+def sample_blocks(nb: int, count: int = 8, seed: int = 1234):
+    """Query blocks the oracle checks: first, last (ragged), middle and seeded random ones."""
+    rng = np.random.default_rng(seed)
+    fixed = [0, nb - 1, nb // 2]
+    rest = [int(b) for b in rng.choice(np.setdiff1d(np.arange(nb), fixed), size=max(0, count - 3), replace=False)]
+    return sorted(set(fixed + rest))[:count]
+
+
+def executed_flops(mask: np.ndarray, N: int, block: int = 128, d: int = 96) -> float:
+    """4 d sum over kept (i, j) block pairs of |B_i| |B_j|."""
+    nb = mask.shape[1]
+    sizes = np.full(nb, block, dtype=np.float64)
+    sizes[-1] = N - (nb - 1) * block
+    per_head = np.einsum("hij,i,j->h", mask.astype(np.float64), sizes, sizes)
+    return float(4.0 * d * per_head.sum())
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=5)
+    ap.add_argument("--warmup", type=int, default=2)
+    ap.add_argument("--workload", default="v5", choices=sorted(DESCR))
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--calib-copy", action="store_true",
+                    help="also run one plain 1 GiB device copy (HBM counter calibration)")
+    ap.add_argument("--traffic", default=os.path.join(ROOT, "profiles", "traffic_dense_v5.json"))
+    args = ap.parse_args()
+
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU only: the path has no multi-GPU mode (heads would shard "
+              "across GPUs with one all-to-all each way; not built).", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import image_diffusion_transformer_amd as dit
+    from synth import WORKLOADS, make_inputs
+
+    wl = WORKLOADS[args.workload]
+    dev = torch.device("cuda:0")
+    t0 = time.time()
+    x = make_inputs(wl)
+    log(f"inputs {wl.name}: N={wl.N} heads={wl.heads} generated in {time.time() - t0:.1f}s")
+
+    def up(b):
+        return torch.from_numpy(b.bits.view(np.int16)).to(dev).view(torch.bfloat16)
+
+    q, k, v = up(x.q), up(x.k), up(x.v)
+    wq, wk = torch.from_numpy(x.wq).to(dev), torch.from_numpy(x.wk).to(dev)
+    g = (wl.T, wl.H, wl.W)
+    o = torch.empty_like(q)
+    ws = dit.workspace_for(q, g)
+    sparse = wl.mode == "sparse"
+    mask = torch.empty((wl.heads, wl.nb, wl.nb), dtype=torch.uint8, device=dev) if sparse else None
+    stream = torch.cuda.current_stream()
+    N, H, d = wl.N, wl.heads, 96
+    dense_flops = 4.0 * N * N * d * H
+
+    def step(ev=None):
+        if sparse:
+            if ev is not None:
+                ev[0].record(stream)
+            dit.dit_attn_route(q, k, wq, wk, g, wl.sparsity, wl.theta, wl.eps, mask=mask, workspace=ws)
+            if ev is not None:
+                ev[1].record(stream)
+            dit.dit_attn_block_sparse(q, k, v, wq, wk, g, mask, wl.theta, wl.eps, o=o, workspace=ws)
+            if ev is not None:
+                ev[2].record(stream)
+        else:
+            if ev is not None:
+                ev[0].record(stream)
+            dit.dit_attn_dense(q, k, v, wq, wk, g, wl.theta, wl.eps, o=o, workspace=ws)
+            if ev is not None:
+                ev[1].record(stream)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    nev = 3 if sparse else 2
+    events = [[torch.cuda.Event(enable_timing=True) for _ in range(nev)] for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t_start = time.perf_counter()
+    for i in range(args.steps):
+        step(events[i])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t_start
+    ms_step = wall * 1e3 / args.steps
+    if sparse:
+        ms_route = float(np.mean([e[0].elapsed_time(e[1]) for e in events]))
+        ms_attn = float(np.mean([e[1].elapsed_time(e[2]) for e in events]))
+    else:
+        ms_attn = float(np.mean([e[0].elapsed_time(e[1]) for e in events]))
+        ms_route = 0.0
+    log(f"timed {args.steps} steps: {ms_step:.2f} ms/step (events: attn {ms_attn:.2f} ms, route {ms_route:.2f} ms)")
+
+    if args.calib_copy:
+        a = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
+        b = torch.empty_like(a)
+        b.copy_(a)
+        torch.cuda.synchronize()
+        del a, b
+
+    if sparse:
+        mask_np = mask.cpu().numpy()
+        flops = executed_flops(mask_np, N)
+    else:
+        mask_np = None
+        flops = dense_flops
+    tflops = flops / (ms_step * 1e-3) / 1e12
+    attn_tflops = flops / (ms_attn * 1e-3) / 1e12
+
+    traffic = None
+    if not sparse and os.path.exists(args.traffic):
+        with open(args.traffic) as f:
+            tr = json.load(f)
+        if tr.get("workload") == wl.name:
+            traffic = tr.get("bytes_per_launch")
+
+    result = {
+        "metric": METRIC,
+        "value": round(tflops, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 3),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic (seeded N(0,1) bf16 Q/K/V, video grids plus smooth sinusoid component; norm weights 1+0.1N(0,1))",
+        "config": {"workload": f"{wl.name}: {DESCR[wl.name]}", "tokens": N, "heads": H, "head_dim": d,
+                   "grid": [wl.T, wl.H, wl.W], "mode": wl.mode, "sparsity": wl.sparsity if sparse else None},
+        "ms_per_layer": round(ms_step, 3),
+        "frac_of_bf16_peak": round(tflops / PEAK_BF16_TFLOPS, 4),
+        "roofline": {"bound": "mfma", "achieved": round(attn_tflops, 2), "peak": PEAK_BF16_TFLOPS,
+                     "unit": "TFLOP/s", "frac": round(attn_tflops / PEAK_BF16_TFLOPS, 4), "traffic": traffic,
+                     "kernel": "attn_kernel" + ("<sparse>" if sparse else "<dense>"),
+                     "kernel_ms": round(ms_attn, 3), "flops_per_launch": flops},
+    }
+    if sparse:
+        result["dense_equivalent_tflops"] = round(dense_flops / (ms_step * 1e-3) / 1e12, 2)
+        result["route_ms"] = round(ms_route, 3)
+        result["kept_fraction"] = round(float(mask_np.mean()), 4)
+
+    # ---- parity on sampled query blocks and the CPU baseline (fp64 oracle on host cores)
+    blocks = sample_blocks(wl.nb)
+    heads = sorted(set([0, H // 3, (2 * H) // 3, H - 1]))
+    rows = np.concatenate([np.arange(b * 128, min(N, (b + 1) * 128)) for b in blocks])
+    o_np = o[torch.from_numpy(rows).to(dev)][:, heads].float().cpu().numpy()
+    if not args.no_cpu_baseline:
+        from oracle import attention as A
+        try:
+            from threadpoolctl import threadpool_info
+            blas_threads = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
+        except Exception:
+            blas_threads = None
+        cores = len(os.sched_getaffinity(0))
+        oracle_mask = mask_np
+        t0 = time.perf_counter()
+        ref = A.attention(x.q, x.k, x.v, x.wq, x.wk, wl.T, wl.H, wl.W, wl.theta, wl.eps, heads=heads, rows=rows,
+                          mask=oracle_mask)
+        t_cpu = time.perf_counter() - t0
+        frac_rows = (len(rows) * len(heads)) / (N * H)
+        if sparse:
+            sizes = np.full(wl.nb, 128.0)
+            sizes[-1] = N - (wl.nb - 1) * 128
+            sample_flops = 4.0 * d * sum(float(sizes[b] * (mask_np[h, b] * sizes).sum())
+                                         for h in heads for b in blocks)
+        else:
+            sample_flops = 4.0 * d * N * len(rows) * len(heads)
+        cpu_tflops = sample_flops / t_cpu / 1e12
+        err = np.abs(o_np.astype(np.float64) - ref)
+        result["parity"] = {"rows": int(len(rows)), "heads": heads, "blocks": blocks,
+                            "max_abs": float(err.max()), "rel_l2": float(np.linalg.norm(err) / np.linalg.norm(ref)),
+                            "mask_source": "gpu router" if sparse else None}
+        result["cpu_baseline"] = {
+            "value": round(cpu_tflops, 5), "unit": "TFLOP/s", "cores": blas_threads or cores, "kind": "oracle",
+            "sample": (f"fp64 numpy oracle on {len(blocks)} query blocks x {len(heads)} heads "
+                       f"({len(rows)} rows each, all keys): {t_cpu:.1f} s for {frac_rows:.5f} of the layer; "
+                       f"full layer extrapolated to {t_cpu / frac_rows:.0f} s"),
+            "host_cores": cores,
+        }
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

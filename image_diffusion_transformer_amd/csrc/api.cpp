@@ -1,0 +1,292 @@
+// Host side of the C ABI declared in include/dit_attn.h: argument validation,
+// workspace layout, host RoPE tables and kernel launches.  Nothing here computes
+// attention; every arithmetic step of the path runs in the gfx950 kernels.
+#include "dit_attn.h"
+
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+#include <map>
+#include <mutex>
+#include <string>
+#include <tuple>
+#include <vector>
+
+#include "dit_internal.h"
+
+namespace {
+
+thread_local std::string g_err;
+
+dit_status fail(dit_status s, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  std::vsnprintf(buf, sizeof(buf), fmt, ap);
+  va_end(ap);
+  g_err = buf;
+  return s;
+}
+
+dit_status fail_hip(hipError_t e, const char* what) {
+  return fail(DIT_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
+
+struct Shape {
+  int T, H, W, heads;
+  long long N;
+  int nb;
+  int nqt;
+};
+
+struct Layout {
+  size_t tab;        // RoPE table [(T+H+W)][32] f32
+  size_t route_r;    // [2][N][heads] f32
+  size_t route_pool; // [2][heads][nb][96] f32
+  size_t list;       // [heads][nqt][nb] i32
+  size_t list_len;   // [heads][nqt] i32
+  size_t total;
+};
+
+Layout make_layout(const Shape& s) {
+  Layout L{};
+  L.tab = 0;
+  const size_t base = align256((size_t)(s.T + s.H + s.W) * dit::kRopeRow * sizeof(float));
+  const size_t r_bytes = align256(2ull * s.N * s.heads * sizeof(float));
+  const size_t pool_bytes = align256(2ull * s.heads * s.nb * dit::kHeadDim * sizeof(float));
+  L.route_r = base;
+  L.route_pool = base + r_bytes;
+  const size_t list_bytes = align256((size_t)s.heads * s.nqt * s.nb * sizeof(int));
+  const size_t len_bytes = align256((size_t)s.heads * s.nqt * sizeof(int));
+  L.list = base;
+  L.list_len = base + list_bytes;
+  L.total = base + std::max(r_bytes + pool_bytes, list_bytes + len_bytes);
+  return L;
+}
+
+bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
+
+// Shape checks shared by every entry point; fills `s`.
+dit_status check_shape(int T, int H, int W, int heads, int head_dim, Shape& s) {
+  if (T < 1 || H < 1 || W < 1 || heads < 1)
+    return fail(DIT_ERR_INVALID_ARG, "grid and heads must be >= 1 (T=%d H=%d W=%d heads=%d)", T, H, W, heads);
+  if (head_dim != dit::kHeadDim)
+    return fail(DIT_ERR_UNSUPPORTED, "head_dim %d is not supported (only 96)", head_dim);
+  const long long N = (long long)T * H * W;
+  if (N * heads * dit::kHeadDim > 2147483647ll)
+    return fail(DIT_ERR_UNSUPPORTED, "N*heads*head_dim = %lld exceeds 2^31-1 elements", N * heads * dit::kHeadDim);
+  const long long nb = (N + dit::kBlock - 1) / dit::kBlock;
+  if (nb > 32768) return fail(DIT_ERR_UNSUPPORTED, "%lld blocks exceed the router limit of 32768", nb);
+  if ((long long)T + H + W > (1 << 24)) return fail(DIT_ERR_UNSUPPORTED, "grid axes too long");
+  s.T = T;
+  s.H = H;
+  s.W = W;
+  s.heads = heads;
+  s.N = N;
+  s.nb = (int)nb;
+  const int bq = dit::attn_query_tile();
+  s.nqt = (int)((N + bq - 1) / bq);
+  return DIT_OK;
+}
+
+dit_status check_common(const void* q, const void* k, const float* wq, const float* wk, float theta, float eps) {
+  if (!q || !k || !wq || !wk) return fail(DIT_ERR_INVALID_ARG, "null q, k, wq or wk");
+  if (!aligned16(q) || !aligned16(k) || !aligned16(wq) || !aligned16(wk))
+    return fail(DIT_ERR_INVALID_ARG, "q, k, wq and wk must be 16-byte aligned");
+  if (!std::isfinite(theta) || theta <= 0.f) return fail(DIT_ERR_INVALID_ARG, "rope_theta must be finite and > 0");
+  if (!std::isfinite(eps) || eps < 0.f) return fail(DIT_ERR_INVALID_ARG, "eps must be finite and >= 0");
+  return DIT_OK;
+}
+
+dit_status check_workspace(const Shape& s, void* ws, size_t ws_bytes, Layout& L) {
+  L = make_layout(s);
+  if (!ws) return fail(DIT_ERR_WORKSPACE, "workspace is null (need %zu bytes)", L.total);
+  if (ws_bytes < L.total) return fail(DIT_ERR_WORKSPACE, "workspace has %zu bytes, need %zu", ws_bytes, L.total);
+  if (((uintptr_t)ws & 255u) != 0) return fail(DIT_ERR_INVALID_ARG, "workspace must be 256-byte aligned");
+  return DIT_OK;
+}
+
+// cos / sin of pos * theta^(-2i/32) per axis position, angle in double, C library cos/sin,
+// rounded once to float.  Rows: t in [0,T), then T + h, then T + H + w; each row 16 cos then 16 sin.
+std::mutex g_tab_mu;
+std::map<std::tuple<int, int, int, uint32_t>, std::vector<float>> g_tabs;
+
+const std::vector<float>& rope_table(int T, int H, int W, float theta) {
+  uint32_t tb;
+  std::memcpy(&tb, &theta, 4);
+  std::lock_guard<std::mutex> lk(g_tab_mu);
+  auto key = std::make_tuple(T, H, W, tb);
+  auto it = g_tabs.find(key);
+  if (it != g_tabs.end()) return it->second;
+  std::vector<float> tab((size_t)(T + H + W) * dit::kRopeRow);
+  const int npos[3] = {T, H, W};
+  int row = 0;
+  for (int a = 0; a < 3; ++a) {
+    for (int p = 0; p < npos[a]; ++p, ++row) {
+      for (int i = 0; i < dit::kPairs; ++i) {
+        const double inv = std::pow((double)theta, -2.0 * i / (double)dit::kAxisDim);
+        const double ang = (double)p * inv;
+        tab[(size_t)row * dit::kRopeRow + i] = (float)std::cos(ang);
+        tab[(size_t)row * dit::kRopeRow + dit::kPairs + i] = (float)std::sin(ang);
+      }
+    }
+  }
+  return g_tabs.emplace(key, std::move(tab)).first->second;
+}
+
+dit_status upload_table(const Shape& s, float theta, void* ws, const Layout& L, hipStream_t st) {
+  const std::vector<float>& tab = rope_table(s.T, s.H, s.W, theta);
+  hipError_t e = hipMemcpyAsync((char*)ws + L.tab, tab.data(), tab.size() * sizeof(float), hipMemcpyHostToDevice, st);
+  if (e != hipSuccess) return fail_hip(e, "hipMemcpyAsync(rope table)");
+  return DIT_OK;
+}
+
+dit::GridDesc grid_desc(const Shape& s) {
+  dit::GridDesc g;
+  g.N = (int)s.N;
+  g.T = s.T;
+  g.H = s.H;
+  g.W = s.W;
+  g.heads = s.heads;
+  g.div_w = dit::make_fastdiv((uint32_t)s.W);
+  g.div_hw = dit::make_fastdiv((uint32_t)s.H * (uint32_t)s.W);
+  return g;
+}
+
+dit::AttnArgs attn_args(const Shape& s, const void* q, const void* k, const void* v, const float* wq, const float* wk,
+                        float eps, void* o, void* ws, const Layout& L) {
+  dit::AttnArgs a{};
+  a.q = (const uint16_t*)q;
+  a.k = (const uint16_t*)k;
+  a.v = (const uint16_t*)v;
+  a.wq = wq;
+  a.wk = wk;
+  a.rope = (const float*)((const char*)ws + L.tab);
+  a.o = (uint16_t*)o;
+  a.g = grid_desc(s);
+  a.qscale = (float)(1.4426950408889634 / std::sqrt((double)dit::kHeadDim));
+  a.eps = eps;
+  a.nqt = s.nqt;
+  a.total = s.heads * s.nqt;
+  a.per_xcd = (a.total + 7) / 8;
+  a.nb = s.nb;
+  return a;
+}
+
+int keep_count(int nb, float sparsity) {
+  const double k = (double)nb - std::floor((double)sparsity * nb + 1e-9);
+  return (int)std::max(1.0, std::min((double)nb, k));
+}
+
+}  // namespace
+
+extern "C" {
+
+size_t dit_attn_workspace_bytes(int T, int H, int W, int heads, int head_dim, int block) {
+  Shape s;
+  std::string saved = g_err;
+  const dit_status st = check_shape(T, H, W, heads, head_dim, s);
+  g_err = saved;
+  if (st != DIT_OK || block != dit::kBlock) return 0;
+  return make_layout(s).total;
+}
+
+int dit_attn_keep_count(int nb, float sparsity) {
+  if (nb < 1 || !std::isfinite(sparsity) || sparsity < 0.f || sparsity >= 1.f) return -1;
+  return keep_count(nb, sparsity);
+}
+
+dit_status dit_attn_dense(const void* q, const void* k, const void* v, const float* wq, const float* wk, int T, int H,
+                          int W, int heads, int head_dim, float rope_theta, float eps, void* o, void* workspace,
+                          size_t workspace_bytes, void* hip_stream) {
+  g_err.clear();
+  Shape s;
+  dit_status st = check_shape(T, H, W, heads, head_dim, s);
+  if (st != DIT_OK) return st;
+  if ((st = check_common(q, k, wq, wk, rope_theta, eps)) != DIT_OK) return st;
+  if (!v || !o) return fail(DIT_ERR_INVALID_ARG, "null v or o");
+  if (!aligned16(v) || !aligned16(o)) return fail(DIT_ERR_INVALID_ARG, "v and o must be 16-byte aligned");
+  Layout L;
+  if ((st = check_workspace(s, workspace, workspace_bytes, L)) != DIT_OK) return st;
+  hipStream_t stream = (hipStream_t)hip_stream;
+  if ((st = upload_table(s, rope_theta, workspace, L, stream)) != DIT_OK) return st;
+  const dit::AttnArgs a = attn_args(s, q, k, v, wq, wk, eps, o, workspace, L);
+  const hipError_t e = dit::launch_attn_dense(a, stream);
+  if (e != hipSuccess) return fail_hip(e, "attention kernel launch");
+  return DIT_OK;
+}
+
+dit_status dit_attn_route(const void* q, const void* k, const float* wq, const float* wk, int T, int H, int W,
+                          int heads, int head_dim, float rope_theta, float eps, float sparsity, int block,
+                          unsigned char* mask, void* workspace, size_t workspace_bytes, void* hip_stream) {
+  g_err.clear();
+  Shape s;
+  dit_status st = check_shape(T, H, W, heads, head_dim, s);
+  if (st != DIT_OK) return st;
+  if (block != dit::kBlock) return fail(DIT_ERR_UNSUPPORTED, "block %d is not supported (only 128)", block);
+  if ((st = check_common(q, k, wq, wk, rope_theta, eps)) != DIT_OK) return st;
+  if (!std::isfinite(sparsity) || sparsity < 0.f || sparsity >= 1.f)
+    return fail(DIT_ERR_INVALID_ARG, "sparsity must be in [0, 1)");
+  if (!mask) return fail(DIT_ERR_INVALID_ARG, "null mask");
+  Layout L;
+  if ((st = check_workspace(s, workspace, workspace_bytes, L)) != DIT_OK) return st;
+  hipStream_t stream = (hipStream_t)hip_stream;
+  if ((st = upload_table(s, rope_theta, workspace, L, stream)) != DIT_OK) return st;
+  dit::RouteArgs a{};
+  a.q = (const uint16_t*)q;
+  a.k = (const uint16_t*)k;
+  a.wq = wq;
+  a.wk = wk;
+  a.rope = (const float*)((const char*)workspace + L.tab);
+  a.g = grid_desc(s);
+  a.eps = eps;
+  a.nb = s.nb;
+  a.keep = keep_count(s.nb, sparsity);
+  a.r = (float*)((char*)workspace + L.route_r);
+  a.pooled = (float*)((char*)workspace + L.route_pool);
+  a.mask = mask;
+  const hipError_t e = dit::launch_route(a, stream);
+  if (e != hipSuccess) return fail_hip(e, "router kernel launch");
+  return DIT_OK;
+}
+
+dit_status dit_attn_block_sparse(const void* q, const void* k, const void* v, const float* wq, const float* wk, int T,
+                                 int H, int W, int heads, int head_dim, float rope_theta, float eps, int block,
+                                 const unsigned char* mask, void* o, void* workspace, size_t workspace_bytes,
+                                 void* hip_stream) {
+  g_err.clear();
+  Shape s;
+  dit_status st = check_shape(T, H, W, heads, head_dim, s);
+  if (st != DIT_OK) return st;
+  if (block != dit::kBlock) return fail(DIT_ERR_UNSUPPORTED, "block %d is not supported (only 128)", block);
+  if ((st = check_common(q, k, wq, wk, rope_theta, eps)) != DIT_OK) return st;
+  if (!v || !o || !mask) return fail(DIT_ERR_INVALID_ARG, "null v, o or mask");
+  if (!aligned16(v) || !aligned16(o)) return fail(DIT_ERR_INVALID_ARG, "v and o must be 16-byte aligned");
+  Layout L;
+  if ((st = check_workspace(s, workspace, workspace_bytes, L)) != DIT_OK) return st;
+  hipStream_t stream = (hipStream_t)hip_stream;
+  if ((st = upload_table(s, rope_theta, workspace, L, stream)) != DIT_OK) return st;
+  dit::CompactArgs c{};
+  c.mask = mask;
+  c.list = (int*)((char*)workspace + L.list);
+  c.list_len = (int*)((char*)workspace + L.list_len);
+  c.heads = s.heads;
+  c.nb = s.nb;
+  c.nqt = s.nqt;
+  c.group = dit::attn_query_tile() / dit::kBlock;
+  hipError_t e = dit::launch_compact(c, stream);
+  if (e != hipSuccess) return fail_hip(e, "mask compaction launch");
+  dit::AttnArgs a = attn_args(s, q, k, v, wq, wk, eps, o, workspace, L);
+  a.list = c.list;
+  a.list_len = c.list_len;
+  e = dit::launch_attn_sparse(a, stream);
+  if (e != hipSuccess) return fail_hip(e, "sparse attention kernel launch");
+  return DIT_OK;
+}
+
+const char* dit_attn_last_error(void) { return g_err.c_str(); }
+
+}  // extern "C"

@@ -1,0 +1,88 @@
+// Internal interface between the host API (api.cpp) and the gfx950 kernels.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace dit {
+
+constexpr int kHeadDim = 96;     // 5376 hidden / 56 heads
+constexpr int kBlock = 128;      // router block and KV tile: 128 consecutive tokens
+constexpr int kAxisDim = 32;     // RoPE channels per axis (t, h, w)
+constexpr int kPairs = 16;       // RoPE pairs per axis
+constexpr int kRopeRow = 32;     // floats per RoPE table row: 16 cos then 16 sin
+
+// Exact unsigned division of n < 2^31 by a runtime divisor d >= 1:
+// q = (n * m) >> s with s = 32 + ceil(log2 d), m = ceil(2^s / d) (fits in 33 bits).
+struct FastDiv {
+  uint64_t m;
+  uint32_t s;
+  uint32_t d;
+};
+
+inline FastDiv make_fastdiv(uint32_t d) {
+  uint32_t l = 0;
+  while ((1ull << l) < d) ++l;
+  FastDiv f;
+  f.s = 32 + l;
+  f.m = (((unsigned __int128)1 << f.s) + d - 1) / d;
+  f.d = d;
+  return f;
+}
+
+struct GridDesc {
+  int N, T, H, W, heads;
+  FastDiv div_w, div_hw;
+};
+
+struct AttnArgs {
+  const uint16_t* q;      // bf16 bits [N][heads][96]
+  const uint16_t* k;
+  const uint16_t* v;
+  const float* wq;        // [96]
+  const float* wk;
+  const float* rope;      // [(T+H+W)][32]: row t, then T+h, then T+H+w; cos[16], sin[16]
+  uint16_t* o;
+  GridDesc g;
+  float qscale;           // log2(e) / sqrt(96): softmax runs in base 2
+  float eps;
+  int nqt;                // query tiles per head
+  int total;              // heads * nqt
+  int per_xcd;            // ceil(total / 8)
+  // block-sparse iteration lists (null for dense)
+  const int* list;        // [heads][nqt][nb]: kv block | (router-block flags << 24)
+  const int* list_len;    // [heads][nqt]
+  int nb;
+};
+
+struct RouteArgs {
+  const uint16_t* q;
+  const uint16_t* k;
+  const float* wq;
+  const float* wk;
+  const float* rope;
+  GridDesc g;
+  float eps;
+  int nb;
+  int keep;
+  float* r;               // [2][N][heads] reciprocal RMS of q (0) and k (1)
+  float* pooled;          // [2][heads][nb][96] block means of q (0) and k (1)
+  unsigned char* mask;    // [heads][nb][nb]
+};
+
+struct CompactArgs {
+  const unsigned char* mask;   // [heads][nb][nb]
+  int* list;                   // [heads][nqt][nb]
+  int* list_len;               // [heads][nqt]
+  int heads, nb, nqt, group;   // group = router blocks per query tile
+};
+
+// Query tile of the attention kernel (tokens per workgroup) -- a multiple of kBlock.
+int attn_query_tile();
+
+hipError_t launch_attn_dense(const AttnArgs& a, hipStream_t s);
+hipError_t launch_attn_sparse(const AttnArgs& a, hipStream_t s);
+hipError_t launch_compact(const CompactArgs& a, hipStream_t s);
+hipError_t launch_route(const RouteArgs& a, hipStream_t s);
+
+}  // namespace dit

@@ -1,0 +1,114 @@
+/*
+ * dit_attn.h -- C ABI of the MI355X (gfx950) DiT self-attention hot path.
+ *
+ * One DiT self-attention layer of MiniMax H3 / H3-Image inference: per-head
+ * QK-RMSNorm and 3D (t, h, w) RoPE applied to Q and K as they are loaded, then
+ * bidirectional (non-causal) softmax attention over the whole token grid, with
+ * an optional block-sparse mode driven by a block router.
+ *
+ * Sources (pages as titled; sections named on each page):
+ *  - H3 SGLang report (CocoLoop, "MiniMax-H3 in SGLang-Diffusion on 8x H200"),
+ *    section on the three stacked acceleration tiers: the fused-operator paragraph
+ *    names QK-RMSNorm with 3D RoPE; the SubBlock-Sparse-Attention paragraph
+ *    describes a block-wise router that prunes KV blocks at sparsity 0.75 / 0.80;
+ *    the limits section restricts that mode to long, non-causal BF16 attention.
+ *  - H3-Image spec table (52hbtv.com), "DiT" row: 56 heads, hidden 5376
+ *    (head dim 96), 3D multimodal RoPE.
+ *
+ * Conventions shared by every entry point
+ *  - N = T * H * W tokens; token n sits at t = n / (H*W), h = (n / W) % H,
+ *    w = n % W (row-major flattening of the grid).
+ *  - q, k, v, o: bfloat16, shape [N][heads][head_dim], contiguous, device memory.
+ *  - wq, wk: float32 [head_dim] RMSNorm weights, shared by all heads, device memory.
+ *  - RMSNorm: x * w / sqrt(mean_c(x_c^2) + eps) over the head_dim channels of
+ *    one (token, head).  RoPE: channels [0,32) rotate with t, [32,64) with h,
+ *    [64,96) with w; pairs (2i, 2i+1); angle pos * rope_theta^(-2i/32); the
+ *    pair (a, b) becomes (a cos - b sin, a sin + b cos).  V is untouched.
+ *  - Attention: O = softmax(Q^ K^T / sqrt(head_dim)) V, every query sees every key.
+ *  - Only head_dim == 96 and block == 128 are implemented (DIT_ERR_UNSUPPORTED
+ *    otherwise).
+ *  - All pointers are owned by the caller.  The library allocates no device
+ *    memory; scratch space comes from `workspace` (see dit_attn_workspace_bytes).
+ *  - Every call is asynchronous on `hip_stream` (a hipStream_t; NULL means the
+ *    null stream) and returns as soon as its work is queued.  Nothing is
+ *    synchronised, printed or thrown across the ABI.
+ *  - Arguments are validated on the host before anything is queued; on error
+ *    no work is queued and dit_attn_last_error() describes the problem.
+ *  - q, k, v, o, mask and workspace must not overlap.  Calls that share a
+ *    workspace must be ordered on one stream.
+ */
+#ifndef DIT_ATTN_H
+#define DIT_ATTN_H
+
+#include <stddef.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  DIT_OK = 0,
+  DIT_ERR_INVALID_ARG = 1, /* null pointer, bad size, non-finite theta/eps, sparsity outside [0,1) */
+  DIT_ERR_UNSUPPORTED = 2, /* head_dim != 96, block != 128, grid too large for one call       */
+  DIT_ERR_WORKSPACE = 3,   /* workspace missing or smaller than dit_attn_workspace_bytes()    */
+  DIT_ERR_HIP = 4          /* a HIP runtime call failed; the HIP error string is in last_error */
+} dit_status;
+
+/* Bytes of device workspace that dense, route and block_sparse need for this
+ * shape (the maximum over the three).  Returns 0 if the shape is invalid. */
+size_t dit_attn_workspace_bytes(int T, int H, int W, int heads, int head_dim, int block);
+
+/* Number of KV blocks each query block keeps at `sparsity`:
+ * nb - floor(sparsity * nb + 1e-9), clamped to [1, nb], where nb = ceil(N / block).
+ * Returns -1 for invalid arguments. */
+int dit_attn_keep_count(int nb, float sparsity);
+
+/* Dense attention.  Writes o [N][heads][head_dim] bf16.
+ * Fused in one kernel: RMSNorm + RoPE of Q and K on load, S = Q^K^T with bf16
+ * MFMA (fp32 accumulate), online softmax in fp32, O += P V with bf16 MFMA,
+ * O / rowsum rounded to bf16. */
+dit_status dit_attn_dense(const void* q, const void* k, const void* v,
+                          const float* wq, const float* wk,
+                          int T, int H, int W, int heads, int head_dim,
+                          float rope_theta, float eps,
+                          void* o,
+                          void* workspace, size_t workspace_bytes, void* hip_stream);
+
+/* Block router.  Writes mask [heads][nb][nb] uint8 (1 = KV block j kept for
+ * query block i), nb = ceil(N / block), the last block holding the remainder.
+ * Per (head, block) it mean-pools the post-RMSNorm, post-RoPE q and k in fp32,
+ * scores block pairs by their dot product, forces the diagonal to +inf and keeps
+ * the dit_attn_keep_count(nb, sparsity) highest-scoring KV blocks per query block,
+ * lower index first on equal scores.  Every fp32 operation is done in one fixed
+ * order with IEEE round-to-nearest and no fused multiply-add, so the mask is
+ * reproducible bit for bit (sequential channel sums, sequential token sums,
+ * correctly rounded division and square root, host-computed cos/sin tables). */
+dit_status dit_attn_route(const void* q, const void* k,
+                          const float* wq, const float* wk,
+                          int T, int H, int W, int heads, int head_dim,
+                          float rope_theta, float eps, float sparsity, int block,
+                          unsigned char* mask,
+                          void* workspace, size_t workspace_bytes, void* hip_stream);
+
+/* Block-sparse attention restricted to the kept KV blocks of `mask`
+ * ([heads][nb][nb] uint8, any 0/1 content, e.g. from dit_attn_route or another
+ * source).  Keys of dropped blocks are never loaded; the softmax renormalises
+ * over the kept keys.  A query block that keeps no KV block gets O = 0.
+ * With an all-ones mask the result equals dit_attn_dense bit for bit. */
+dit_status dit_attn_block_sparse(const void* q, const void* k, const void* v,
+                                 const float* wq, const float* wk,
+                                 int T, int H, int W, int heads, int head_dim,
+                                 float rope_theta, float eps, int block,
+                                 const unsigned char* mask,
+                                 void* o,
+                                 void* workspace, size_t workspace_bytes, void* hip_stream);
+
+/* Text of the last error on the calling thread ("" if the last call succeeded).
+ * Valid until the next call on the same thread. */
+const char* dit_attn_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* DIT_ATTN_H */
