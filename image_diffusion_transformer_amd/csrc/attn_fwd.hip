@@ -47,10 +47,16 @@ constexpr int KROW = 104;     // bf16 per K^ row in LDS: 208 B (odd multiple of 
 constexpr int VROW = 96;      // bf16 per V row in LDS: 192 B: conflict-free transposing reads
 constexpr float kTau = 8.0f;  // lazy-rescale threshold, base-2 log units
 
-// Kernel shape: 4 waves (one per SIMD), 2 query blocks of 32 per wave.
-constexpr int kNW = 4;
-constexpr int kQB = 2;
-constexpr int kBQ = kNW * kQB * 32;   // 256 queries per workgroup
+// Kernel shape: kNW waves per workgroup, kQB blocks of 32 queries per wave.
+#ifndef DIT_ATTN_NW
+#define DIT_ATTN_NW 8
+#endif
+#ifndef DIT_ATTN_QB
+#define DIT_ATTN_QB 2
+#endif
+constexpr int kNW = DIT_ATTN_NW;
+constexpr int kQB = DIT_ATTN_QB;
+constexpr int kBQ = kNW * kQB * 32;   // queries per workgroup
 
 __device__ __forceinline__ uint32_t fastdiv(uint32_t n, const FastDiv& f) {
   return (uint32_t)(((uint64_t)n * f.m) >> f.s);
@@ -139,7 +145,7 @@ __device__ __forceinline__ void load_kv_raw(const AttnArgs& a, int head, int til
 template <int TPK, int CPT>
 __device__ __forceinline__ void stage_kv(const AttnArgs& a, int tile, int kk, int sub,
                                          const u32x4 (&kr)[CPT], const u32x4 (&vr)[CPT],
-                                         uint16_t* sK, uint16_t* sV) {
+                                         const float* wk, uint16_t* sK, uint16_t* sV) {
   const int n = tile * BK + kk;
   float ss = 0.f;
 #pragma unroll
@@ -158,7 +164,7 @@ __device__ __forceinline__ void stage_kv(const AttnArgs& a, int tile, int kk, in
   for (int j = 0; j < CPT; ++j) {
     const int c = sub + TPK * j;
     const float* rp = a.rope + rope_row(a.g, c >> 2, t, h, w) * kRopeRow;
-    const u32x4 y = norm_rope_chunk(kr[j], r, 1.0f, rp, c, a.wk);
+    const u32x4 y = norm_rope_chunk(kr[j], r, 1.0f, rp, c, wk);
     *(u32x4*)(sK + kk * KROW + 8 * c) = live ? y : u32x4{0, 0, 0, 0};
     *(u32x4*)(sV + kk * VROW + 8 * c) = vr[j];
   }
@@ -181,7 +187,30 @@ __device__ __forceinline__ bf16x8 load_vt(const uint16_t* sV, int kb, int s, int
   return __builtin_bit_cast(bf16x8, v);
 }
 
-template <int NW, int QB, bool SPARSE>
+// Softmax modes.  QK-RMSNorm bounds every logit: |q^ . k^| / sqrt(96) <= sqrt(96) max|w_q| max|w_k|
+// (RoPE preserves norms).  When that bound, in base-2 units, is at most kStaticBound, exp2(S) with
+// no shift can neither overflow nor underflow for any input, and the shift cancels in O / rowsum:
+// no running max, no subtraction, no rescale.  Otherwise the online (running-max) softmax runs.
+enum SoftmaxMode { kStatic = 0, kOnline = 1 };
+constexpr float kStaticBound = 48.0f;
+
+__device__ __forceinline__ bool static_bound_holds(const AttnArgs& a, int lane) {
+  float mq = 0.f, mk = 0.f;
+  for (int i = lane; i < kHeadDim; i += 64) {
+    mq = fmaxf(mq, fabsf(a.wq[i]));
+    mk = fmaxf(mk, fabsf(a.wk[i]));
+  }
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) {
+    mq = fmaxf(mq, __shfl_xor(mq, o));
+    mk = fmaxf(mk, __shfl_xor(mk, o));
+  }
+  // |q^|, |k^| <= sqrt(96) max|w| (RMS <= 1 after the norm); 1.02 covers rsq, rotation and bf16 rounding.
+  const float bound = 1.4426950408889634f * 9.797958971132712f * mq * mk * 1.02f;
+  return bound <= kStaticBound;   // false for NaN weights
+}
+
+template <int NW, int QB, bool SPARSE, int MODE>
 __global__ void __launch_bounds__(NW * 64) attn_kernel(AttnArgs a) {
   constexpr int NT = NW * 64;
   constexpr int BQ = NW * QB * 32;
@@ -191,12 +220,18 @@ __global__ void __launch_bounds__(NW * 64) attn_kernel(AttnArgs a) {
   static_assert(BQ % BK == 0, "query tile must hold whole router blocks");
   __shared__ __attribute__((aligned(16))) uint16_t sK[2 * BK * KROW];
   __shared__ __attribute__((aligned(16))) uint16_t sV[2 * BK * VROW];
+  // K's norm weights live in LDS: read once per tile there instead of being held in registers.
+  __shared__ __attribute__((aligned(16))) float sWk[kHeadDim];
 
   const int logical = (int)(blockIdx.x & 7) * a.per_xcd + (int)(blockIdx.x >> 3);
   if (logical >= a.total) return;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  // Both softmax kernels are launched; the one whose mode does not apply exits here.
+  if (static_bound_holds(a, lane) != (MODE == kStatic)) return;
+  if (tid < kHeadDim) sWk[tid] = a.wk[tid];
+  __syncthreads();
   const int head = logical / a.nqt;
   const int qt = logical - head * a.nqt;
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int half = lane >> 5, l32 = lane & 31;
   const int N = a.g.N;
   const int rb = (wave * QB * 32) / BK;   // router block of this wave inside the query tile
@@ -256,7 +291,7 @@ __global__ void __launch_bounds__(NW * 64) attn_kernel(AttnArgs a) {
   if (ntiles > 0) {
     const int t0 = SPARSE ? (lst[0] & 0xffffff) : 0;
     load_kv_raw<TPK, CPT>(a, head, t0, kk, sub, kr, vr);
-    stage_kv<TPK, CPT>(a, t0, kk, sub, kr, vr, sK, sV);
+    stage_kv<TPK, CPT>(a, t0, kk, sub, kr, vr, sWk, sK, sV);
   }
   __syncthreads();
 
@@ -300,21 +335,24 @@ __global__ void __launch_bounds__(NW * 64) attn_kernel(AttnArgs a) {
         bf16x8 P[QB][2];
 #pragma unroll
         for (int qb = 0; qb < QB; ++qb) {
-          float mx = S[qb][0];
+          if constexpr (MODE == kOnline) {
+            float mx = S[qb][0];
 #pragma unroll
-          for (int i = 1; i < 16; ++i) mx = fmaxf(mx, S[qb][i]);
-          mx = pair_max(mx);
-          if (__builtin_amdgcn_ballot_w64(mx > m[qb] + kTau)) {
-            const float mn = fmaxf(m[qb], mx);
-            const float alpha = __builtin_amdgcn_exp2f(m[qb] - mn);
-            l[qb] *= alpha;
+            for (int i = 1; i < 16; ++i) mx = fmaxf(mx, S[qb][i]);
+            mx = pair_max(mx);
+            if (__builtin_amdgcn_ballot_w64(mx > m[qb] + kTau)) {
+              const float mn = fmaxf(m[qb], mx);
+              const float alpha = __builtin_amdgcn_exp2f(m[qb] - mn);
+              l[qb] *= alpha;
 #pragma unroll
-            for (int db = 0; db < 3; ++db) acc[qb][db] *= alpha;
-            m[qb] = mn;
+              for (int db = 0; db < 3; ++db) acc[qb][db] *= alpha;
+              m[qb] = mn;
+            }
           }
           float p[16];
 #pragma unroll
-          for (int i = 0; i < 16; ++i) p[i] = __builtin_amdgcn_exp2f(S[qb][i] - m[qb]);
+          for (int i = 0; i < 16; ++i)
+            p[i] = __builtin_amdgcn_exp2f(MODE == kOnline ? S[qb][i] - m[qb] : S[qb][i]);
           // Packed pairs kept in scalar variables: bit-casting an element of a u32x4 to bf16x2
           // mis-selects the element in this toolchain (every dot2 then reads element 0).
           uint32_t w[8];
@@ -340,7 +378,7 @@ __global__ void __launch_bounds__(NW * 64) attn_kernel(AttnArgs a) {
       }
     }
     if (has_next)
-      stage_kv<TPK, CPT>(a, ntile, kk, sub, kr, vr, sK + (st ^ 1) * BK * KROW, sV + (st ^ 1) * BK * VROW);
+      stage_kv<TPK, CPT>(a, ntile, kk, sub, kr, vr, sWk, sK + (st ^ 1) * BK * KROW, sV + (st ^ 1) * BK * VROW);
     __syncthreads();
   }
 
@@ -399,7 +437,12 @@ __global__ void __launch_bounds__(256) compact_kernel(CompactArgs a) {
 template <bool SPARSE>
 hipError_t launch_attn(const AttnArgs& a, hipStream_t s) {
   const int blocks = a.per_xcd * 8;
-  hipLaunchKernelGGL((attn_kernel<kNW, kQB, SPARSE>), dim3(blocks), dim3(kNW * 64), 0, s, a);
+  // Both softmax kernels are queued; each checks the weight bound itself and the one that does
+  // not apply returns before touching any data.
+  hipLaunchKernelGGL((attn_kernel<kNW, kQB, SPARSE, kStatic>), dim3(blocks), dim3(kNW * 64), 0, s, a);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL((attn_kernel<kNW, kQB, SPARSE, kOnline>), dim3(blocks), dim3(kNW * 64), 0, s, a);
   return hipGetLastError();
 }
 
