@@ -1,0 +1,105 @@
+"""Full-size GPU parity, in the launch configuration the bench times, on outputs the oracle can
+compute one query block at a time: sampled query blocks of sampled heads for O, and complete
+[nb, nb] router masks for sampled heads (bit-exact)."""
+import numpy as np
+import pytest
+import torch
+
+import image_diffusion_transformer_amd as dit
+from oracle import attention as A
+from oracle import router as R
+from synth import WORKLOADS, make_inputs
+
+pytestmark = pytest.mark.gpu
+DEV = torch.device("cuda:0")
+MAX_ABS, REL_L2 = 2e-2, 1e-2
+
+
+def upload(x):
+    def t(b):
+        return torch.from_numpy(b.bits.view(np.int16)).to(DEV).view(torch.bfloat16)
+    return (t(x.q), t(x.k), t(x.v), torch.from_numpy(x.wq).to(DEV), torch.from_numpy(x.wk).to(DEV))
+
+
+def sample_rows(nb, N, count=3, seed=1234):
+    rng = np.random.default_rng(seed)
+    blocks = sorted(set([0, nb - 1] + [int(b) for b in rng.choice(np.arange(1, nb - 1), size=count - 2,
+                                                                   replace=False)]))
+    return blocks, np.concatenate([np.arange(b * 128, min(N, (b + 1) * 128)) for b in blocks])
+
+
+def check(got, ref, what):
+    err = np.abs(got.astype(np.float64) - ref)
+    rel = float(np.linalg.norm(err) / np.linalg.norm(ref))
+    print(f"{what}: max_abs={err.max():.3e} rel_l2={rel:.3e}", flush=True)
+    assert np.all(np.isfinite(got)) and err.max() <= MAX_ABS and rel <= REL_L2, (what, err.max(), rel)
+
+
+@pytest.fixture(scope="module")
+def v5():
+    x = make_inputs("v5")
+    return x, upload(x)
+
+
+@pytest.mark.parametrize("name", ["image", "v5"])
+def test_dense_full_size_sampled(name, v5):
+    x, (q, k, v, wq, wk) = v5 if name == "v5" else (lambda x: (x, upload(x)))(make_inputs(name))
+    wl = x.workload
+    print(f"case dense full {name} N={wl.N}", flush=True)
+    o = dit.dit_attn_dense(q, k, v, wq, wk, (wl.T, wl.H, wl.W), wl.theta, wl.eps)
+    torch.cuda.synchronize()
+    blocks, rows = sample_rows(wl.nb, wl.N)
+    heads = [0, 29, 55]
+    got = o[torch.from_numpy(rows).to(DEV)][:, heads].float().cpu().numpy()
+    ref = A.attention(x.q, x.k, x.v, x.wq, x.wk, wl.T, wl.H, wl.W, wl.theta, wl.eps, heads=heads, rows=rows)
+    check(got, ref, f"dense {name} blocks {blocks}")
+
+
+def test_route_and_sparse_full_size_v5(v5):
+    x, (q, k, v, wq, wk) = v5
+    wl = WORKLOADS["v5s"]
+    g = (wl.T, wl.H, wl.W)
+    print("case route+sparse full v5s", flush=True)
+    ws = dit.workspace_for(q, g)
+    mask = dit.dit_attn_route(q, k, wq, wk, g, wl.sparsity, wl.theta, wl.eps, workspace=ws)
+    o = dit.dit_attn_block_sparse(q, k, v, wq, wk, g, mask, wl.theta, wl.eps, workspace=ws)
+    torch.cuda.synchronize()
+    heads = [0, 55]
+    m_gpu = mask.cpu().numpy()
+    keep = R.keep_count(wl.nb, wl.sparsity)
+    assert np.all(m_gpu.sum(axis=2) == keep)
+    m_ref = R.route_mask(x.q, x.k, x.wq, x.wk, wl.T, wl.H, wl.W, wl.sparsity, wl.theta, wl.eps, heads=heads)
+    for i, hd in enumerate(heads):
+        bad = np.nonzero(np.any(m_gpu[hd] != m_ref[i], axis=1))[0]
+        assert bad.size == 0, f"head {hd}: {bad.size} router rows differ, first {bad[:5].tolist()}"
+    # sparse O on the (verified) oracle mask for the sampled heads
+    blocks, rows = sample_rows(wl.nb, wl.N)
+    got = o[torch.from_numpy(rows).to(DEV)][:, heads].float().cpu().numpy()
+    full_mask = np.zeros_like(m_gpu)
+    full_mask[heads] = m_ref
+    ref = A.attention(x.q, x.k, x.v, x.wq, x.wk, wl.T, wl.H, wl.W, wl.theta, wl.eps, heads=heads, rows=rows,
+                      mask=full_mask)
+    check(got, ref, f"sparse v5s blocks {blocks}")
+
+
+def test_route_and_sparse_full_size_v10():
+    wl = WORKLOADS["v10s"]
+    x = make_inputs(wl)
+    q, k, v, wq, wk = upload(x)
+    g = (wl.T, wl.H, wl.W)
+    print("case route+sparse full v10s", flush=True)
+    ws = dit.workspace_for(q, g)
+    mask = dit.dit_attn_route(q, k, wq, wk, g, wl.sparsity, wl.theta, wl.eps, workspace=ws)
+    o = dit.dit_attn_block_sparse(q, k, v, wq, wk, g, mask, wl.theta, wl.eps, workspace=ws)
+    torch.cuda.synchronize()
+    heads = [17]
+    m_gpu = mask.cpu().numpy()
+    m_ref = R.route_mask(x.q, x.k, x.wq, x.wk, wl.T, wl.H, wl.W, wl.sparsity, wl.theta, wl.eps, heads=heads)
+    assert np.array_equal(m_gpu[17], m_ref[0])
+    blocks, rows = sample_rows(wl.nb, wl.N, count=2)
+    got = o[torch.from_numpy(rows).to(DEV)][:, heads].float().cpu().numpy()
+    full_mask = np.zeros_like(m_gpu)
+    full_mask[heads] = m_ref
+    ref = A.attention(x.q, x.k, x.v, x.wq, x.wk, wl.T, wl.H, wl.W, wl.theta, wl.eps, heads=heads, rows=rows,
+                      mask=full_mask)
+    check(got, ref, f"sparse v10s blocks {blocks}")
