@@ -44,6 +44,7 @@ struct Shape {
 
 struct Layout {
   size_t tab;        // RoPE table [(T+H+W)][32] f32
+  size_t kvf;        // K^ / V^T fragment images [heads][nb] x 48 KB (dense and block-sparse)
   size_t route_r;    // [2][N][heads] f32
   size_t route_pool; // [2][heads][nb][96] f32
   size_t list;       // [heads][nqt][nb] i32
@@ -54,7 +55,8 @@ struct Layout {
 Layout make_layout(const Shape& s) {
   Layout L{};
   L.tab = 0;
-  const size_t base = align256((size_t)(s.T + s.H + s.W) * dit::kRopeRow * sizeof(float));
+  L.kvf = align256((size_t)(s.T + s.H + s.W) * dit::kRopeRow * sizeof(float));
+  const size_t base = L.kvf + (size_t)s.heads * s.nb * dit::kTileImageBytes;
   const size_t r_bytes = align256(2ull * s.N * s.heads * sizeof(float));
   const size_t pool_bytes = align256(2ull * s.heads * s.nb * dit::kHeadDim * sizeof(float));
   L.route_r = base;
@@ -165,6 +167,7 @@ dit::AttnArgs attn_args(const Shape& s, const void* q, const void* k, const void
   a.wq = wq;
   a.wk = wk;
   a.rope = (const float*)((const char*)ws + L.tab);
+  a.kvf = (uint16_t*)((char*)ws + L.kvf);
   a.o = (uint16_t*)o;
   a.g = grid_desc(s);
   a.qscale = (float)(1.4426950408889634 / std::sqrt((double)dit::kHeadDim));

@@ -5,26 +5,31 @@
 // non-causal attention; its SubBlock-Sparse-Attention paragraph prunes whole KV
 // blocks.  Head shape (56 heads x 96) from the H3-Image spec table, DiT row.
 //
-// Design (one kernel for dense and block-sparse):
-//  * Work is split per (head, query tile of NW*QB*32 tokens); the launch index is
-//    remapped so the workgroups resident on one XCD walk the same head's K/V and
-//    share its L2.
+// Design (the same kernels serve dense and block-sparse):
+//  * A bandwidth-bound prepass normalises and rotates every K row once per layer
+//    and writes K^ and V, per (head, 128-key tile), as a 48 KB image of MFMA
+//    operand fragments (64 lanes x 16 bytes each).  The attention kernel then
+//    stages a KV tile with 48 plain global->LDS copies and no vector ALU work,
+//    which leaves the VALU to the softmax.
+//  * Attention work is split per (head, query tile of NW*QB*32 tokens); the launch
+//    index is remapped so the workgroups resident on one XCD walk the same head's
+//    K/V and share its L2.
 //  * Each wave owns QB blocks of 32 queries.  Its Q rows are loaded once (two
 //    lanes per query, 48 channels each), RMS-normalised, rotated, scaled by
 //    log2(e)/sqrt(96) and kept in registers as bf16 MFMA B operands.
-//  * K/V stream through LDS in tiles of 128 keys, double-buffered: while a tile is
-//    consumed, the next tile's raw rows are already in registers; K rows are then
-//    RMS-normalised and rotated once per workgroup and written as bf16, V rows are
-//    copied as they are.
+//  * KV tiles are double-buffered in LDS: the next tile's fragment image is in
+//    flight (global->LDS, no registers) while the current one is consumed.
 //  * S^T = K^ Q^T with v_mfma_f32_32x32x16_bf16 (keys on rows, queries on columns):
 //    each lane holds one query column, so the softmax row statistics need only
 //    in-lane reductions plus one permlane32 swap, and the S^T accumulator is
 //    already the B operand of the next MFMA after bf16 packing.
-//  * O^T += V^T P^T with the same MFMA; V^T fragments come straight from the
-//    row-major V tile through ds_read_b64_tr_b16 (transposing LDS reads).
-//  * Online softmax in base 2 with a lazy rescale: the running max only moves
-//    (and O, l are rescaled) when a block max exceeds it by more than 8, so
-//    exp2 arguments stay <= 8; the final O / l is exact for any stale max.
+//  * O^T += V^T P^T with the same MFMA, V^T fragments read from LDS with one
+//    16-byte load per lane.
+//  * Static-shift softmax when the QK-RMSNorm logit bound allows it (p = exp2(S),
+//    no running max); otherwise an online softmax in base 2 with a lazy rescale:
+//    the running max only moves (and O, l are rescaled) when a block max exceeds
+//    it by more than 8, so exp2 arguments stay <= 8; the final O / l is exact for
+//    any stale max.
 //  * Row sums accumulate the bf16-rounded probabilities (v_dot2_f32_bf16), the
 //    same values the PV product uses.
 #include "dit_internal.h"
@@ -40,12 +45,23 @@ typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef float f32x2 __attribute__((ext_vector_type(2)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
-typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
 
 constexpr int BK = kBlock;    // keys per KV tile (= router block)
-constexpr int KROW = 104;     // bf16 per K^ row in LDS: 208 B (odd multiple of 16 B): conflict-free b128 reads
-constexpr int VROW = 96;      // bf16 per V row in LDS: 192 B: conflict-free transposing reads
 constexpr float kTau = 8.0f;  // lazy-rescale threshold, base-2 log units
+
+// Fragment image of one (head, 128-key tile), written by kv_prep_kernel: 48 fragments of 512 bf16
+// (lane l owns elements 8l..8l+7).
+//   fragment kb*6 + ks        (K^, 0..23):  lane l holds K^[32kb + l%32][16ks + 8(l/32) + e], e = 0..7:
+//                             the A operand of S^T for key sub-block kb, channel step ks.
+//   fragment 24 + (2kb+s)*3 + db (V^T, 24..47): lane l holds V[key][32db + l%32] for the keys
+//                             32kb + 16s + 4(l/32) + {0, 1, 2, 3, 8, 9, 10, 11}: the A operand of
+//                             O^T for channel block db, k-step s of sub-block kb.  That key order is
+//                             the one in which the S^T accumulator holds the probabilities.
+// Keys past the grid have zero K^ and V.
+constexpr int kFrag = 512;
+constexpr int kVFrag0 = 24;
+constexpr int kTileFrags = 48;
+constexpr int kTileElems = kTileFrags * kFrag;   // 24576 bf16 = 48 KB
 
 // Kernel shape: kNW waves per workgroup, kQB blocks of 32 queries per wave.
 #ifndef DIT_ATTN_NW
@@ -87,14 +103,6 @@ __device__ __forceinline__ float pair_sum(float x) {
   return __uint_as_float(r[0]) + __uint_as_float(r[1]);
 }
 
-// Sum over groups of TPK adjacent lanes (TPK in {1, 2, 4}); every lane of a group gets the same bits.
-template <int TPK>
-__device__ __forceinline__ float group_sum(float x) {
-  if constexpr (TPK >= 2) x += __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), 0xB1, 0xF, 0xF, true));
-  if constexpr (TPK >= 4) x += __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), 0x4E, 0xF, 0xF, true));
-  return x;
-}
-
 __device__ __forceinline__ int rope_row(const GridDesc& g, int axis, int t, int h, int w) {
   return axis == 0 ? t : (axis == 1 ? g.T + h : g.T + g.H + w);
 }
@@ -117,74 +125,6 @@ __device__ __forceinline__ u32x4 norm_rope_chunk(u32x4 raw, float r, float scale
     out[e] = pack_bf16(ye * scale, yf * scale);
   }
   return out;
-}
-
-template <int TPK, int CPT>
-__device__ __forceinline__ void load_kv_raw(const AttnArgs& a, int head, int tile, int kk, int sub,
-                                            u32x4 (&kr)[CPT], u32x4 (&vr)[CPT]) {
-  const int n = tile * BK + kk;
-  if (n < a.g.N) {
-    const size_t base = ((size_t)n * a.g.heads + head) * kHeadDim;
-    const u32x4* kp = (const u32x4*)(a.k + base);
-    const u32x4* vp = (const u32x4*)(a.v + base);
-#pragma unroll
-    for (int j = 0; j < CPT; ++j) {
-      kr[j] = kp[sub + TPK * j];
-      vr[j] = vp[sub + TPK * j];
-    }
-  } else {
-#pragma unroll
-    for (int j = 0; j < CPT; ++j) {
-      kr[j] = u32x4{0, 0, 0, 0};
-      vr[j] = u32x4{0, 0, 0, 0};
-    }
-  }
-}
-
-// Normalise + rotate this thread's K chunks and write K^ and V into one LDS stage.
-template <int TPK, int CPT>
-__device__ __forceinline__ void stage_kv(const AttnArgs& a, int tile, int kk, int sub,
-                                         const u32x4 (&kr)[CPT], const u32x4 (&vr)[CPT],
-                                         const float* wk, uint16_t* sK, uint16_t* sV) {
-  const int n = tile * BK + kk;
-  float ss = 0.f;
-#pragma unroll
-  for (int j = 0; j < CPT; ++j)
-#pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      const float lo = bf_lo(kr[j][e]), hi = bf_hi(kr[j][e]);
-      ss += lo * lo + hi * hi;
-    }
-  ss = group_sum<TPK>(ss);
-  const bool live = n < a.g.N;
-  const float r = live ? __builtin_amdgcn_rsqf(ss * (1.0f / kHeadDim) + a.eps) : 0.f;
-  int t = 0, h = 0, w = 0;
-  if (live) grid_pos((uint32_t)n, a.g, t, h, w);
-#pragma unroll
-  for (int j = 0; j < CPT; ++j) {
-    const int c = sub + TPK * j;
-    const float* rp = a.rope + rope_row(a.g, c >> 2, t, h, w) * kRopeRow;
-    const u32x4 y = norm_rope_chunk(kr[j], r, 1.0f, rp, c, wk);
-    *(u32x4*)(sK + kk * KROW + 8 * c) = live ? y : u32x4{0, 0, 0, 0};
-    *(u32x4*)(sV + kk * VROW + 8 * c) = vr[j];
-  }
-}
-
-// V^T fragment (A operand, 32 channels x 16 keys) for k-step s of key sub-block kb, channel block db.
-// Lane group g = lane/16 covers channels d0..d0+15 of half hh = g/2; k-slots 0..3 of the half are keys
-// base+0..3, k-slots 4..7 keys base+8..11 (matching where S^T keeps those keys).
-__device__ __forceinline__ bf16x8 load_vt(const uint16_t* sV, int kb, int s, int db, int lane) {
-  const int g = lane >> 4, i = lane & 15;
-  const int d0 = db * 32 + 16 * (g & 1);
-  const int key = kb * 32 + 16 * s + 4 * (g >> 1) + (i >> 2);
-  const int col = d0 + 4 * (i & 3);
-  const lds_s16x4* p0 = (const lds_s16x4*)(sV + key * VROW + col);
-  const lds_s16x4* p1 = (const lds_s16x4*)(sV + (key + 8) * VROW + col);
-  const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)p0);
-  const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)p1);
-  typedef short s16x8 __attribute__((ext_vector_type(8)));
-  const s16x8 v = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
-  return __builtin_bit_cast(bf16x8, v);
 }
 
 // Softmax modes.  QK-RMSNorm bounds every logit: |q^ . k^| / sqrt(96) <= sqrt(96) max|w_q| max|w_k|
@@ -210,47 +150,15 @@ __device__ __forceinline__ bool static_bound_holds(const AttnArgs& a, int lane) 
   return bound <= kStaticBound;   // false for NaN weights
 }
 
-template <int NW, int QB, bool SPARSE, int MODE>
-__global__ void __launch_bounds__(NW * 64) attn_kernel(AttnArgs a) {
-  constexpr int NT = NW * 64;
-  constexpr int BQ = NW * QB * 32;
-  constexpr int TPK = NT / BK;        // threads per key row while staging
-  constexpr int CPT = 12 / TPK;       // 16-byte chunks per thread per tensor
-  static_assert(TPK * BK == NT && CPT * TPK == 12, "staging layout");
-  static_assert(BQ % BK == 0, "query tile must hold whole router blocks");
-  __shared__ __attribute__((aligned(16))) uint16_t sK[2 * BK * KROW];
-  __shared__ __attribute__((aligned(16))) uint16_t sV[2 * BK * VROW];
-  // K's norm weights live in LDS: read once per tile there instead of being held in registers.
-  __shared__ __attribute__((aligned(16))) float sWk[kHeadDim];
-
-  const int logical = (int)(blockIdx.x & 7) * a.per_xcd + (int)(blockIdx.x >> 3);
-  if (logical >= a.total) return;
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  // Both softmax kernels are launched; the one whose mode does not apply exits here.
-  if (static_bound_holds(a, lane) != (MODE == kStatic)) return;
-  if (tid < kHeadDim) sWk[tid] = a.wk[tid];
-  __syncthreads();
-  const int head = logical / a.nqt;
-  const int qt = logical - head * a.nqt;
+// Q fragments of the wave: load, RMSNorm, RoPE, scale by log2(e)/sqrt(96), pack to bf16 (once per query).
+template <int QB, int BQ>
+__device__ __forceinline__ void load_q(const AttnArgs& a, int head, int qt, int wave, int lane,
+                                       bf16x8 (&qf)[QB][6]) {
   const int half = lane >> 5, l32 = lane & 31;
-  const int N = a.g.N;
-  const int rb = (wave * QB * 32) / BK;   // router block of this wave inside the query tile
-
-  int ntiles;
-  const int* lst = nullptr;
-  if constexpr (SPARSE) {
-    ntiles = a.list_len[logical];
-    lst = a.list + (size_t)logical * a.nb;
-  } else {
-    ntiles = (N + BK - 1) / BK;
-  }
-
-  // ---- Q: load, RMSNorm, RoPE, scale, pack (once per query) ----
-  bf16x8 qf[QB][6];
 #pragma unroll
   for (int qb = 0; qb < QB; ++qb) {
     const int n = qt * BQ + (wave * QB + qb) * 32 + l32;
-    const bool live = n < N;
+    const bool live = n < a.g.N;
     u32x4 raw[6];
     const size_t base = ((size_t)(live ? n : 0) * a.g.heads + head) * kHeadDim;
 #pragma unroll
@@ -275,120 +183,116 @@ __global__ void __launch_bounds__(NW * 64) attn_kernel(AttnArgs a) {
       qf[qb][ks] = __builtin_bit_cast(bf16x8, norm_rope_chunk(raw[ks], r, a.qscale, rp, c, a.wq));
     }
   }
+}
 
-  f32x16 acc[QB][3];
-  float m[QB], l[QB];
+// S^T for key sub-block kb (32 keys) against the wave's QB query blocks: 6 K^ fragments, 6*QB MFMAs.
+template <int QB>
+__device__ __forceinline__ void qk_block(const uint16_t* T_, int kb, int lane, const bf16x8 (&qf)[QB][6],
+                                         f32x16 (&S)[QB]) {
+#pragma unroll
+  for (int qb = 0; qb < QB; ++qb) S[qb] = f32x16{};
+#pragma unroll
+  for (int ks = 0; ks < 6; ++ks) {
+    const bf16x8 ka = *(const bf16x8*)(T_ + (kb * 6 + ks) * kFrag + lane * 8);
+#pragma unroll
+    for (int qb = 0; qb < QB; ++qb) S[qb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka, qf[qb][ks], S[qb], 0, 0, 0);
+  }
+}
+
+// O^T += V^T P^T for key sub-block kb: 6 V^T fragments, 6*QB MFMAs.
+template <int QB>
+__device__ __forceinline__ void pv_block(const uint16_t* T_, int kb, int lane, const bf16x8 (&P)[QB][2],
+                                         f32x16 (&acc)[QB][3]) {
+#pragma unroll
+  for (int s = 0; s < 2; ++s)
+#pragma unroll
+    for (int db = 0; db < 3; ++db) {
+      const bf16x8 va = *(const bf16x8*)(T_ + (kVFrag0 + (2 * kb + s) * 3 + db) * kFrag + lane * 8);
+#pragma unroll
+      for (int qb = 0; qb < QB; ++qb)
+        acc[qb][db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va, P[qb][s], acc[qb][db], 0, 0, 0);
+    }
+}
+
+// Pack 16 probabilities of one query block as two bf16x8 PV operands and add their bf16 values to l.
+__device__ __forceinline__ void pack_probs(const float (&p)[16], float& l, bf16x8 (&P)[2]) {
+  // Packed pairs kept in scalar variables: bit-casting an element of a u32x4 to bf16x2
+  // mis-selects the element in this toolchain (every dot2 then reads element 0).
+  uint32_t w[8];
+#pragma unroll
+  for (int e = 0; e < 8; ++e) w[e] = pack_bf16(p[2 * e], p[2 * e + 1]);
+  const bf16x2 one = {(__bf16)1.0f, (__bf16)1.0f};
+  float ls = l;
+#pragma unroll
+  for (int e = 0; e < 8; ++e) ls = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, w[e]), one, ls, false);
+  l = ls;
+  P[0] = __builtin_bit_cast(bf16x8, u32x4{w[0], w[1], w[2], w[3]});
+  P[1] = __builtin_bit_cast(bf16x8, u32x4{w[4], w[5], w[6], w[7]});
+}
+
+// Key k of register i in a lane's S^T fragment of sub-block kb: kb*32 + 8*(i/4) + 4*(lane/32) + i%4.
+__device__ __forceinline__ bool key_live(int key0, int i, int half, int N) {
+  return key0 + 8 * (i >> 2) + 4 * half + (i & 3) < N;
+}
+
+// Online (running-max) softmax of one sub-block; keys >= N get probability 0.
+template <int QB>
+__device__ __forceinline__ void softmax_online(f32x16 (&S)[QB], bool ragged, int key0, int N, int lane,
+                                               float (&m)[QB], float (&l)[QB], f32x16 (&acc)[QB][3],
+                                               bf16x8 (&P)[QB][2]) {
+  const int half = lane >> 5;
+  if (ragged) {
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      const bool live = key_live(key0, i, half, N);
+#pragma unroll
+      for (int qb = 0; qb < QB; ++qb) S[qb][i] = live ? S[qb][i] : -INFINITY;
+    }
+  }
 #pragma unroll
   for (int qb = 0; qb < QB; ++qb) {
-    m[qb] = -1e30f;
-    l[qb] = 0.f;
+    float mx = S[qb][0];
 #pragma unroll
-    for (int db = 0; db < 3; ++db) acc[qb][db] = f32x16{};
-  }
-
-  const int kk = tid / TPK, sub = tid % TPK;
-  u32x4 kr[CPT], vr[CPT];
-  if (ntiles > 0) {
-    const int t0 = SPARSE ? (lst[0] & 0xffffff) : 0;
-    load_kv_raw<TPK, CPT>(a, head, t0, kk, sub, kr, vr);
-    stage_kv<TPK, CPT>(a, t0, kk, sub, kr, vr, sWk, sK, sV);
-  }
-  __syncthreads();
-
-  for (int it = 0; it < ntiles; ++it) {
-    const int st = it & 1;
-    int tile = it, flags = 0xff;
-    if constexpr (SPARSE) {
-      const int e = lst[it];
-      tile = e & 0xffffff;
-      flags = e >> 24;
+    for (int i = 1; i < 16; ++i) mx = fmaxf(mx, S[qb][i]);
+    mx = pair_max(mx);
+    if (__builtin_amdgcn_ballot_w64(mx > m[qb] + kTau)) {
+      const float mn = fmaxf(m[qb], mx);
+      const float alpha = __builtin_amdgcn_exp2f(m[qb] - mn);
+      l[qb] *= alpha;
+#pragma unroll
+      for (int db = 0; db < 3; ++db) acc[qb][db] *= alpha;
+      m[qb] = mn;
     }
-    const bool has_next = it + 1 < ntiles;
-    const int ntile = has_next ? (SPARSE ? (lst[it + 1] & 0xffffff) : it + 1) : 0;
-    if (has_next) load_kv_raw<TPK, CPT>(a, head, ntile, kk, sub, kr, vr);
-
-    if ((flags >> rb) & 1) {
-      const uint16_t* K_ = sK + st * BK * KROW;
-      const uint16_t* V_ = sV + st * BK * VROW;
-      const bool ragged = (tile + 1) * BK > N;
-#pragma unroll 1
-      for (int kb = 0; kb < BK / 32; ++kb) {
-        f32x16 S[QB];
+    float p[16];
 #pragma unroll
-        for (int qb = 0; qb < QB; ++qb) S[qb] = f32x16{};
-#pragma unroll
-        for (int ks = 0; ks < 6; ++ks) {
-          const bf16x8 ka = *(const bf16x8*)(K_ + (kb * 32 + l32) * KROW + 16 * ks + 8 * half);
-#pragma unroll
-          for (int qb = 0; qb < QB; ++qb)
-            S[qb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka, qf[qb][ks], S[qb], 0, 0, 0);
-        }
-        if (ragged) {
-#pragma unroll
-          for (int i = 0; i < 16; ++i) {
-            const int key = tile * BK + kb * 32 + 8 * (i >> 2) + 4 * half + (i & 3);
-            if (key >= N)
-#pragma unroll
-              for (int qb = 0; qb < QB; ++qb) S[qb][i] = -INFINITY;
-          }
-        }
-        bf16x8 P[QB][2];
-#pragma unroll
-        for (int qb = 0; qb < QB; ++qb) {
-          if constexpr (MODE == kOnline) {
-            float mx = S[qb][0];
-#pragma unroll
-            for (int i = 1; i < 16; ++i) mx = fmaxf(mx, S[qb][i]);
-            mx = pair_max(mx);
-            if (__builtin_amdgcn_ballot_w64(mx > m[qb] + kTau)) {
-              const float mn = fmaxf(m[qb], mx);
-              const float alpha = __builtin_amdgcn_exp2f(m[qb] - mn);
-              l[qb] *= alpha;
-#pragma unroll
-              for (int db = 0; db < 3; ++db) acc[qb][db] *= alpha;
-              m[qb] = mn;
-            }
-          }
-          float p[16];
-#pragma unroll
-          for (int i = 0; i < 16; ++i)
-            p[i] = __builtin_amdgcn_exp2f(MODE == kOnline ? S[qb][i] - m[qb] : S[qb][i]);
-          // Packed pairs kept in scalar variables: bit-casting an element of a u32x4 to bf16x2
-          // mis-selects the element in this toolchain (every dot2 then reads element 0).
-          uint32_t w[8];
-#pragma unroll
-          for (int e = 0; e < 8; ++e) w[e] = pack_bf16(p[2 * e], p[2 * e + 1]);
-          const bf16x2 one = {(__bf16)1.0f, (__bf16)1.0f};
-          float ls = l[qb];
-#pragma unroll
-          for (int e = 0; e < 8; ++e) ls = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, w[e]), one, ls, false);
-          l[qb] = ls;
-          P[qb][0] = __builtin_bit_cast(bf16x8, u32x4{w[0], w[1], w[2], w[3]});
-          P[qb][1] = __builtin_bit_cast(bf16x8, u32x4{w[4], w[5], w[6], w[7]});
-        }
-#pragma unroll
-        for (int s = 0; s < 2; ++s)
-#pragma unroll
-          for (int db = 0; db < 3; ++db) {
-            const bf16x8 va = load_vt(V_, kb, s, db, lane);
-#pragma unroll
-            for (int qb = 0; qb < QB; ++qb)
-              acc[qb][db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va, P[qb][s], acc[qb][db], 0, 0, 0);
-          }
-      }
-    }
-    if (has_next)
-      stage_kv<TPK, CPT>(a, ntile, kk, sub, kr, vr, sWk, sK + (st ^ 1) * BK * KROW, sV + (st ^ 1) * BK * VROW);
-    __syncthreads();
+    for (int i = 0; i < 16; ++i) p[i] = __builtin_amdgcn_exp2f(S[qb][i] - m[qb]);
+    pack_probs(p, l[qb], P[qb]);
   }
+}
 
-  // ---- epilogue: O = acc / l, bf16 RNE ----
+// Static-shift softmax of one sub-block: p = exp2(S).  Keys past the grid (zero K^ and V) give S = 0 and
+// p = 1; they add nothing to O and the kernel takes their count off the row sum at the end.
+template <int QB>
+__device__ __forceinline__ void softmax_static(const f32x16 (&S)[QB], float (&l)[QB], bf16x8 (&P)[QB][2]) {
 #pragma unroll
   for (int qb = 0; qb < QB; ++qb) {
-    const int n = qt * BQ + (wave * QB + qb) * 32 + l32;
+    float p[16];
+#pragma unroll
+    for (int i = 0; i < 16; ++i) p[i] = __builtin_amdgcn_exp2f(S[qb][i]);
+    pack_probs(p, l[qb], P[qb]);
+  }
+}
+
+template <int QB>
+__device__ __forceinline__ void store_o(const AttnArgs& a, int head, int n0, int lane, const f32x16 (&acc)[QB][3],
+                                        const float (&l)[QB]) {
+  const int half = lane >> 5, l32 = lane & 31;
+#pragma unroll
+  for (int qb = 0; qb < QB; ++qb) {
+    const int n = n0 + qb * 32 + l32;
     const float lt = pair_sum(l[qb]);
     const float inv = lt > 0.f ? 1.0f / lt : 0.f;
-    if (n < N) {
+    if (n < a.g.N) {
       uint16_t* op = a.o + ((size_t)n * a.g.heads + head) * kHeadDim;
 #pragma unroll
       for (int db = 0; db < 3; ++db)
@@ -402,6 +306,222 @@ __global__ void __launch_bounds__(NW * 64) attn_kernel(AttnArgs a) {
         }
     }
   }
+}
+
+// Shared setup of both kernels: workgroup -> (head, query tile) with the XCD-aware order, tile list.
+struct TileIter {
+  int head, qt, ntiles;
+  const int* lst;
+  __device__ __forceinline__ int tile(int it, bool sparse) const { return sparse ? (lst[it] & 0xffffff) : it; }
+  __device__ __forceinline__ int flags(int it, bool sparse) const { return sparse ? (lst[it] >> 24) : 0xff; }
+};
+
+template <bool SPARSE>
+__device__ __forceinline__ bool tile_iter(const AttnArgs& a, TileIter& ti) {
+  const int logical = (int)(blockIdx.x & 7) * a.per_xcd + (int)(blockIdx.x >> 3);
+  if (logical >= a.total) return false;
+  ti.head = logical / a.nqt;
+  ti.qt = logical - ti.head * a.nqt;
+  if constexpr (SPARSE) {
+    ti.ntiles = a.list_len[logical];
+    ti.lst = a.list + (size_t)logical * a.nb;
+  } else {
+    ti.ntiles = (a.g.N + BK - 1) / BK;
+    ti.lst = nullptr;
+  }
+  return true;
+}
+
+// ------------------------------------------------------------------------------------------------
+// K^ / V fragment prepass: one workgroup per (128-key tile, head).  The tile's raw K and V rows are read
+// with coalesced 16-byte loads into LDS; each K row is RMS-normalised and rotated (two threads per row,
+// six 8-channel chunks each) and every fragment lane slot is written with one 16-byte store.
+__global__ void __launch_bounds__(256) kv_prep_kernel(AttnArgs a) {
+  __shared__ __attribute__((aligned(16))) uint16_t rk[BK * kHeadDim];
+  __shared__ __attribute__((aligned(16))) uint16_t rv[BK * kHeadDim];
+  __shared__ __attribute__((aligned(16))) float sW[kHeadDim];
+  const int tile = blockIdx.x, head = blockIdx.y, tid = threadIdx.x;
+  const int N = a.g.N;
+  if (tid < kHeadDim) sW[tid] = a.wk[tid];
+  for (int i = tid; i < BK * 12; i += 256) {
+    const int row = i / 12, c = i - 12 * row;
+    const int n = tile * BK + row;
+    u32x4 kx = {0, 0, 0, 0}, vx = {0, 0, 0, 0};
+    if (n < N) {
+      const size_t off = ((size_t)n * a.g.heads + head) * kHeadDim + 8 * c;
+      kx = *(const u32x4*)(a.k + off);
+      vx = *(const u32x4*)(a.v + off);
+    }
+    *(u32x4*)(rk + row * kHeadDim + 8 * c) = kx;
+    *(u32x4*)(rv + row * kHeadDim + 8 * c) = vx;
+  }
+  __syncthreads();
+  uint16_t* img = a.kvf + ((size_t)head * a.nb + tile) * kTileElems;
+  {
+    const int kk = tid & (BK - 1), cg = tid >> 7;     // key row; chunks 6cg .. 6cg+5
+    const int n = tile * BK + kk;
+    const bool live = n < N;
+    const u32x4* row = (const u32x4*)(rk + kk * kHeadDim);
+    float ss = 0.f;
+#pragma unroll
+    for (int c = 0; c < 12; ++c) {
+      const u32x4 x = row[c];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const float lo = bf_lo(x[e]), hi = bf_hi(x[e]);
+        ss += lo * lo + hi * hi;
+      }
+    }
+    const float r = live ? __builtin_amdgcn_rsqf(ss * (1.0f / kHeadDim) + a.eps) : 0.f;
+    int t = 0, h = 0, w = 0;
+    if (live) grid_pos((uint32_t)n, a.g, t, h, w);
+#pragma unroll
+    for (int j = 0; j < 6; ++j) {
+      const int c = 6 * cg + j;                        // channels 8c .. 8c+7 = step c/2, lane half c%2
+      const float* rp = a.rope + rope_row(a.g, c >> 2, t, h, w) * kRopeRow;
+      const u32x4 y = norm_rope_chunk(row[c], r, 1.0f, rp, c, sW);
+      *(u32x4*)(img + ((kk >> 5) * 6 + (c >> 1)) * kFrag + ((c & 1) * 32 + (kk & 31)) * 8) =
+          live ? y : u32x4{0, 0, 0, 0};
+    }
+  }
+  for (int i = tid; i < (kTileFrags - kVFrag0) * 64; i += 256) {
+    const int f = i >> 6, l = i & 63;                  // f = (2kb + s)*3 + db
+    const int d = 32 * (f % 3) + (l & 31);
+    const int key0 = 16 * (f / 3) + 4 * (l >> 5);
+    uint32_t w[4];
+#pragma unroll
+    for (int e2 = 0; e2 < 4; ++e2) {
+      const int key = key0 + 2 * e2 + (e2 >= 2 ? 4 : 0);
+      w[e2] = (uint32_t)rv[key * kHeadDim + d] | ((uint32_t)rv[(key + 1) * kHeadDim + d] << 16);
+    }
+    *(u32x4*)(img + (kVFrag0 + f) * kFrag + l * 8) = u32x4{w[0], w[1], w[2], w[3]};
+  }
+}
+
+// This wave's share (fragments 6w .. 6w+5) of one tile's fragment image, copied global -> LDS without
+// passing through registers: lane l of each copy moves the 16 bytes of lane slot l.
+__device__ __forceinline__ void dma_tile(const uint16_t* src, int wave, int lane, uint16_t* dst) {
+  typedef __attribute__((address_space(3))) void lds_void;
+#pragma unroll
+  for (int c = 0; c < 6; ++c) {
+    const int f = 6 * wave + c;
+    __builtin_amdgcn_global_load_lds((const void*)(src + f * kFrag + lane * 8), (lds_void*)(dst + f * kFrag), 16,
+                                     0, 0);
+  }
+}
+
+// Barrier that publishes a tile.  Each wave first waits for its own global->LDS copies (vmcnt(0): the
+// compiler does not relate these copies to later LDS reads and inserts no wait for them) and for its LDS
+// accesses (lgkmcnt(0)); after the barrier every wave's copies have landed.  sched_barrier(0) and the
+// empty asm statements keep the compiler from moving any instruction or memory access across.
+__device__ __forceinline__ void tile_barrier() {
+  __builtin_amdgcn_sched_barrier(0);
+  __builtin_amdgcn_s_waitcnt(0x0070);   // vmcnt(0) lgkmcnt(0)
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_sched_barrier(0);
+}
+
+// ------------------------------------------------------------------------------------------------
+// Attention kernels: 8 waves (2 per SIMD), QB blocks of 32 queries per wave.  Per KV tile: start the copy
+// of the next tile's fragment image into the other LDS stage, then per 32-key sub-block: S MFMAs, softmax,
+// PV MFMAs.  One barrier per tile.
+//
+// Online-softmax kernel, for norm weights whose logit bound is too large for the static shift.
+template <int QB, bool SPARSE>
+__global__ void __launch_bounds__(512) attn_online_kernel(AttnArgs a) {
+  constexpr int NW = 8, BQ = NW * QB * 32, SUB = BK / 32;
+  static_assert(NW * 6 == kTileFrags && BQ % BK == 0, "tile shape");
+  __shared__ __attribute__((aligned(16))) uint16_t sKV[2 * kTileElems];
+  TileIter ti;
+  if (!tile_iter<SPARSE>(a, ti)) return;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  if (static_bound_holds(a, lane)) return;          // the static kernel handles these weights
+  const int N = a.g.N, rb = (wave * QB * 32) / BK, nt = ti.ntiles;
+  const uint16_t* img = a.kvf + (size_t)ti.head * a.nb * kTileElems;
+  if (nt > 0) dma_tile(img + (size_t)ti.tile(0, SPARSE) * kTileElems, wave, lane, sKV);
+  bf16x8 qf[QB][6];
+  load_q<QB, BQ>(a, ti.head, ti.qt, wave, lane, qf);
+  f32x16 acc[QB][3];
+  float m[QB], l[QB];
+#pragma unroll
+  for (int qb = 0; qb < QB; ++qb) {
+    m[qb] = -1e30f;
+    l[qb] = 0.f;
+#pragma unroll
+    for (int db = 0; db < 3; ++db) acc[qb][db] = f32x16{};
+  }
+  tile_barrier();
+  for (int it = 0; it < nt; ++it) {
+    const int st = it & 1, tile = ti.tile(it, SPARSE);
+    if (it + 1 < nt)
+      dma_tile(img + (size_t)ti.tile(it + 1, SPARSE) * kTileElems, wave, lane, sKV + (st ^ 1) * kTileElems);
+    if ((ti.flags(it, SPARSE) >> rb) & 1) {
+      const uint16_t* T_ = sKV + st * kTileElems;
+      const bool ragged = (tile + 1) * BK > N;
+#pragma unroll 1
+      for (int kb = 0; kb < SUB; ++kb) {
+        f32x16 S[QB];
+        qk_block<QB>(T_, kb, lane, qf, S);
+        bf16x8 P[QB][2];
+        softmax_online<QB>(S, ragged, tile * BK + kb * 32, N, lane, m, l, acc, P);
+        pv_block<QB>(T_, kb, lane, P, acc);
+      }
+    }
+    tile_barrier();
+  }
+  store_o<QB>(a, ti.head, ti.qt * BQ + wave * QB * 32, lane, acc, l);
+}
+
+// Static-softmax kernel.  Keys past the grid have zero K^ and V: S = 0 and p = 1 there, they add nothing to
+// O and their count is taken off the row sum at the end -- no masking inside the loop.
+template <int QB, bool SPARSE>
+__global__ void __launch_bounds__(512) attn_static_kernel(AttnArgs a) {
+  constexpr int NW = 8, BQ = NW * QB * 32, SUB = BK / 32;
+  static_assert(NW * 6 == kTileFrags && BQ % BK == 0, "tile shape");
+  __shared__ __attribute__((aligned(16))) uint16_t sKV[2 * kTileElems];
+  TileIter ti;
+  if (!tile_iter<SPARSE>(a, ti)) return;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  if (!static_bound_holds(a, lane)) return;         // the online kernel handles these weights
+  const int N = a.g.N, rb = (wave * QB * 32) / BK, nt = ti.ntiles;
+  const uint16_t* img = a.kvf + (size_t)ti.head * a.nb * kTileElems;
+  if (nt > 0) dma_tile(img + (size_t)ti.tile(0, SPARSE) * kTileElems, wave, lane, sKV);
+  bf16x8 qf[QB][6];
+  load_q<QB, BQ>(a, ti.head, ti.qt, wave, lane, qf);
+  f32x16 acc[QB][3];
+  float l[QB];
+#pragma unroll
+  for (int qb = 0; qb < QB; ++qb) {
+    l[qb] = 0.f;
+#pragma unroll
+    for (int db = 0; db < 3; ++db) acc[qb][db] = f32x16{};
+  }
+  tile_barrier();
+  int pad = 0;                                      // keys past the grid counted in l
+  for (int it = 0; it < nt; ++it) {
+    const int st = it & 1, tile = ti.tile(it, SPARSE);
+    if (it + 1 < nt)
+      dma_tile(img + (size_t)ti.tile(it + 1, SPARSE) * kTileElems, wave, lane, sKV + (st ^ 1) * kTileElems);
+    if ((ti.flags(it, SPARSE) >> rb) & 1) {
+      const uint16_t* T_ = sKV + st * kTileElems;
+#pragma unroll 1
+      for (int kb = 0; kb < SUB; ++kb) {
+        f32x16 S[QB];
+        qk_block<QB>(T_, kb, lane, qf, S);
+        bf16x8 P[QB][2];
+        softmax_static<QB>(S, l, P);
+        pv_block<QB>(T_, kb, lane, P, acc);
+      }
+      pad += max(0, (tile + 1) * BK - N);
+    }
+    tile_barrier();
+  }
+  // Padded keys sit in both lane halves; the row sum over both halves drops them exactly.
+#pragma unroll
+  for (int qb = 0; qb < QB; ++qb) l[qb] -= (lane < 32) ? (float)pad : 0.f;
+  store_o<QB>(a, ti.head, ti.qt * BQ + wave * QB * 32, lane, acc, l);
 }
 
 // Block-sparse iteration lists: for each (head, query tile) the ascending KV blocks kept by any of the
@@ -436,13 +556,16 @@ __global__ void __launch_bounds__(256) compact_kernel(CompactArgs a) {
 
 template <bool SPARSE>
 hipError_t launch_attn(const AttnArgs& a, hipStream_t s) {
+  hipLaunchKernelGGL(kv_prep_kernel, dim3(a.nb, a.g.heads), dim3(256), 0, s, a);
+  hipError_t e0 = hipGetLastError();
+  if (e0 != hipSuccess) return e0;
   const int blocks = a.per_xcd * 8;
   // Both softmax kernels are queued; each checks the weight bound itself and the one that does
   // not apply returns before touching any data.
-  hipLaunchKernelGGL((attn_kernel<kNW, kQB, SPARSE, kStatic>), dim3(blocks), dim3(kNW * 64), 0, s, a);
+  hipLaunchKernelGGL((attn_static_kernel<kQB, SPARSE>), dim3(blocks), dim3(512), 0, s, a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL((attn_kernel<kNW, kQB, SPARSE, kOnline>), dim3(blocks), dim3(kNW * 64), 0, s, a);
+  hipLaunchKernelGGL((attn_online_kernel<kQB, SPARSE>), dim3(blocks), dim3(512), 0, s, a);
   return hipGetLastError();
 }
 

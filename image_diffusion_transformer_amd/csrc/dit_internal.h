@@ -42,6 +42,7 @@ struct AttnArgs {
   const float* wq;        // [96]
   const float* wk;
   const float* rope;      // [(T+H+W)][32]: row t, then T+h, then T+H+w; cos[16], sin[16]
+  uint16_t* kvf;          // [heads][nb][48][512] bf16: K^ / V^T MFMA fragment image per 128-key tile
   uint16_t* o;
   GridDesc g;
   float qscale;           // log2(e) / sqrt(96): softmax runs in base 2
@@ -76,6 +77,9 @@ struct CompactArgs {
   int* list_len;               // [heads][nqt]
   int heads, nb, nqt, group;   // group = router blocks per query tile
 };
+
+// Bytes of one (head, 128-key tile) fragment image: 48 fragments of 64 lanes x 16 bytes.
+constexpr size_t kTileImageBytes = 48 * 1024;
 
 // Query tile of the attention kernel (tokens per workgroup) -- a multiple of kBlock.
 int attn_query_tile();

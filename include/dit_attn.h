@@ -55,7 +55,9 @@ typedef enum {
 } dit_status;
 
 /* Bytes of device workspace that dense, route and block_sparse need for this
- * shape (the maximum over the three).  Returns 0 if the shape is invalid. */
+ * shape (enough for any of the three; about 2 * N * heads * head_dim * 2 bytes
+ * for the K^/V fragment images plus the router's or the sparse lists' share).
+ * Returns 0 if the shape is invalid. */
 size_t dit_attn_workspace_bytes(int T, int H, int W, int heads, int head_dim, int block);
 
 /* Number of KV blocks each query block keeps at `sparsity`:
@@ -64,9 +66,11 @@ size_t dit_attn_workspace_bytes(int T, int H, int W, int heads, int head_dim, in
 int dit_attn_keep_count(int nb, float sparsity);
 
 /* Dense attention.  Writes o [N][heads][head_dim] bf16.
- * Fused in one kernel: RMSNorm + RoPE of Q and K on load, S = Q^K^T with bf16
- * MFMA (fp32 accumulate), online softmax in fp32, O += P V with bf16 MFMA,
- * O / rowsum rounded to bf16. */
+ * Two kernels on `hip_stream`: a prepass that RMS-normalises and rotates every
+ * K row once and writes K^ (bf16) and V into the workspace as MFMA operand
+ * fragments, then the attention kernel: RMSNorm + RoPE of Q on load,
+ * S = Q^K^T with bf16 MFMA (fp32 accumulate), softmax in fp32 (base 2),
+ * O += P V with bf16 MFMA (P rounded to bf16), O / rowsum rounded to bf16. */
 dit_status dit_attn_dense(const void* q, const void* k, const void* v,
                           const float* wq, const float* wk,
                           int T, int H, int W, int heads, int head_dim,

@@ -50,6 +50,7 @@ def test_workspace_bytes(lib):
     N, nb = 124992, 977
     assert n >= 2 * N * 56 * 4 + 2 * 56 * nb * 96 * 4      # router: rms + pooled vectors
     assert n >= 56 * -(-N // 512) * nb * 4                  # sparse: KV lists per 512-token query tile
+    assert n >= 56 * nb * 48 * 1024 + 56 * -(-N // 512) * nb * 4   # K^/V fragment images + sparse lists
     assert dit.dit_attn_workspace_bytes(31, 48, 84, 56, 128) == 0   # head_dim 128 unsupported
     assert dit.dit_attn_workspace_bytes(31, 48, 84, 56, 96, 64) == 0
     assert dit.dit_attn_workspace_bytes(0, 48, 84, 56) == 0
