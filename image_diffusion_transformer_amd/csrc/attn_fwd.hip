@@ -34,6 +34,12 @@
 //    same values the PV product uses.
 #include "dit_internal.h"
 
+// Every floating-point expression here is evaluated as written, without fused multiply-adds the compiler
+// chooses by itself: the choice could differ between the unrolled copies of the same code (for example
+// the two query blocks of a wave), and a query would then round differently depending on which wave and
+// slot computes it.  Fused operations are written out (fmaf) where they are wanted.
+#pragma clang fp contract(off)
+
 namespace dit {
 namespace {
 
@@ -151,13 +157,32 @@ __device__ __forceinline__ bool static_bound_holds(const AttnArgs& a, int lane) 
 }
 
 // Q fragments of the wave: load, RMSNorm, RoPE, scale by log2(e)/sqrt(96), pack to bf16 (once per query).
-template <int QB, int BQ>
+// Query block (32 queries) of the workgroup's tile that block qb of a wave holds.  Dense: wave w holds
+// blocks QB*w .. QB*w+QB-1.  Block-sparse (QB = 2): wave w holds part w%4 of router blocks 2(w/4) and
+// 2(w/4)+1, so each router block's 128 queries are spread over all four SIMDs (waves w and w+4 share
+// SIMD w%4) and a KV tile kept by few router blocks still keeps every SIMD busy.
+template <int QB, bool SPARSE>
+__device__ __forceinline__ int query_block(int wave, int qb) {
+  if constexpr (SPARSE) {
+    static_assert(QB == 2, "sparse mapping assumes 2 blocks per wave");
+    return 8 * (wave >> 2) + 4 * qb + (wave & 3);
+  } else {
+    return wave * QB + qb;
+  }
+}
+// Router block (within the tile) of the wave's query block qb.
+template <int QB, bool SPARSE>
+__device__ __forceinline__ int router_block(int wave, int qb) {
+  return query_block<QB, SPARSE>(wave, qb) >> 2;
+}
+
+template <int QB, int BQ, bool SPARSE>
 __device__ __forceinline__ void load_q(const AttnArgs& a, int head, int qt, int wave, int lane,
                                        bf16x8 (&qf)[QB][6]) {
   const int half = lane >> 5, l32 = lane & 31;
 #pragma unroll
   for (int qb = 0; qb < QB; ++qb) {
-    const int n = qt * BQ + (wave * QB + qb) * 32 + l32;
+    const int n = qt * BQ + query_block<QB, SPARSE>(wave, qb) * 32 + l32;
     const bool live = n < a.g.N;
     u32x4 raw[6];
     const size_t base = ((size_t)(live ? n : 0) * a.g.heads + head) * kHeadDim;
@@ -186,7 +211,8 @@ __device__ __forceinline__ void load_q(const AttnArgs& a, int head, int qt, int 
 }
 
 // S^T for key sub-block kb (32 keys) against the wave's QB query blocks: 6 K^ fragments, 6*QB MFMAs.
-template <int QB>
+// QM: bit qb set = query block qb takes part (block-sparse tiles kept by only some of a wave's blocks).
+template <int QB, int QM = (1 << QB) - 1>
 __device__ __forceinline__ void qk_block(const uint16_t* T_, int kb, int lane, const bf16x8 (&qf)[QB][6],
                                          f32x16 (&S)[QB]) {
 #pragma unroll
@@ -195,12 +221,14 @@ __device__ __forceinline__ void qk_block(const uint16_t* T_, int kb, int lane, c
   for (int ks = 0; ks < 6; ++ks) {
     const bf16x8 ka = *(const bf16x8*)(T_ + (kb * 6 + ks) * kFrag + lane * 8);
 #pragma unroll
-    for (int qb = 0; qb < QB; ++qb) S[qb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka, qf[qb][ks], S[qb], 0, 0, 0);
+    for (int qb = 0; qb < QB; ++qb)
+      if (((QM >> qb) & 1) != 0)
+        S[qb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka, qf[qb][ks], S[qb], 0, 0, 0);
   }
 }
 
 // O^T += V^T P^T for key sub-block kb: 6 V^T fragments, 6*QB MFMAs.
-template <int QB>
+template <int QB, int QM = (1 << QB) - 1>
 __device__ __forceinline__ void pv_block(const uint16_t* T_, int kb, int lane, const bf16x8 (&P)[QB][2],
                                          f32x16 (&acc)[QB][3]) {
 #pragma unroll
@@ -210,7 +238,8 @@ __device__ __forceinline__ void pv_block(const uint16_t* T_, int kb, int lane, c
       const bf16x8 va = *(const bf16x8*)(T_ + (kVFrag0 + (2 * kb + s) * 3 + db) * kFrag + lane * 8);
 #pragma unroll
       for (int qb = 0; qb < QB; ++qb)
-        acc[qb][db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va, P[qb][s], acc[qb][db], 0, 0, 0);
+        if (((QM >> qb) & 1) != 0)
+          acc[qb][db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va, P[qb][s], acc[qb][db], 0, 0, 0);
     }
 }
 
@@ -236,7 +265,7 @@ __device__ __forceinline__ bool key_live(int key0, int i, int half, int N) {
 }
 
 // Online (running-max) softmax of one sub-block; keys >= N get probability 0.
-template <int QB>
+template <int QB, int QM = (1 << QB) - 1>
 __device__ __forceinline__ void softmax_online(f32x16 (&S)[QB], bool ragged, int key0, int N, int lane,
                                                float (&m)[QB], float (&l)[QB], f32x16 (&acc)[QB][3],
                                                bf16x8 (&P)[QB][2]) {
@@ -251,6 +280,7 @@ __device__ __forceinline__ void softmax_online(f32x16 (&S)[QB], bool ragged, int
   }
 #pragma unroll
   for (int qb = 0; qb < QB; ++qb) {
+    if (((QM >> qb) & 1) == 0) continue;
     float mx = S[qb][0];
 #pragma unroll
     for (int i = 1; i < 16; ++i) mx = fmaxf(mx, S[qb][i]);
@@ -272,10 +302,11 @@ __device__ __forceinline__ void softmax_online(f32x16 (&S)[QB], bool ragged, int
 
 // Static-shift softmax of one sub-block: p = exp2(S).  Keys past the grid (zero K^ and V) give S = 0 and
 // p = 1; they add nothing to O and the kernel takes their count off the row sum at the end.
-template <int QB>
+template <int QB, int QM = (1 << QB) - 1>
 __device__ __forceinline__ void softmax_static(const f32x16 (&S)[QB], float (&l)[QB], bf16x8 (&P)[QB][2]) {
 #pragma unroll
   for (int qb = 0; qb < QB; ++qb) {
+    if (((QM >> qb) & 1) == 0) continue;
     float p[16];
 #pragma unroll
     for (int i = 0; i < 16; ++i) p[i] = __builtin_amdgcn_exp2f(S[qb][i]);
@@ -283,13 +314,13 @@ __device__ __forceinline__ void softmax_static(const f32x16 (&S)[QB], float (&l)
   }
 }
 
-template <int QB>
-__device__ __forceinline__ void store_o(const AttnArgs& a, int head, int n0, int lane, const f32x16 (&acc)[QB][3],
-                                        const float (&l)[QB]) {
+template <int QB, int BQ, bool SPARSE>
+__device__ __forceinline__ void store_o(const AttnArgs& a, int head, int qt, int wave, int lane,
+                                        const f32x16 (&acc)[QB][3], const float (&l)[QB]) {
   const int half = lane >> 5, l32 = lane & 31;
 #pragma unroll
   for (int qb = 0; qb < QB; ++qb) {
-    const int n = n0 + qb * 32 + l32;
+    const int n = qt * BQ + query_block<QB, SPARSE>(wave, qb) * 32 + l32;
     const float lt = pair_sum(l[qb]);
     const float inv = lt > 0.f ? 1.0f / lt : 0.f;
     if (n < a.g.N) {
@@ -426,29 +457,52 @@ __device__ __forceinline__ void tile_barrier() {
 // ------------------------------------------------------------------------------------------------
 // Attention kernels: 8 waves (2 per SIMD), QB blocks of 32 queries per wave.  Per KV tile: start the copy
 // of the next tile's fragment image into the other LDS stage, then per 32-key sub-block: S MFMAs, softmax,
-// PV MFMAs.  One barrier per tile.
-//
-// Online-softmax kernel, for norm weights whose logit bound is too large for the static shift.
-template <int QB, bool SPARSE>
-__global__ void __launch_bounds__(512) attn_online_kernel(AttnArgs a) {
-  constexpr int NW = 8, BQ = NW * QB * 32, SUB = BK / 32;
+// PV MFMAs.  One barrier per tile.  Block-sparse tiles are computed only for the query blocks whose
+// router block keeps them (activity mask QM of the wave's two blocks).
+template <int QB, int QM, int MODE>
+__device__ __forceinline__ void tile_body(const uint16_t* T_, int lane, const bf16x8 (&qf)[QB][6],
+                                          f32x16 (&acc)[QB][3], float (&m)[QB], float (&l)[QB], bool ragged,
+                                          int key0, int N) {
+#pragma unroll 1
+  for (int kb = 0; kb < BK / 32; ++kb) {
+    f32x16 S[QB];
+    qk_block<QB, QM>(T_, kb, lane, qf, S);
+    bf16x8 P[QB][2];
+    if constexpr (MODE == kStatic)
+      softmax_static<QB, QM>(S, l, P);
+    else
+      softmax_online<QB, QM>(S, ragged, key0 + kb * 32, N, lane, m, l, acc, P);
+    pv_block<QB, QM>(T_, kb, lane, P, acc);
+  }
+}
+
+// Static mode: keys past the grid have zero K^ and V: S = 0 and p = 1 there, they add nothing to O and
+// their count is taken off the row sum at the end -- no masking inside the loop.  Online mode (for norm
+// weights whose logit bound is too large for the static shift) masks them.
+template <int QB, bool SPARSE, int MODE>
+__device__ __forceinline__ void attn_kernel_body(const AttnArgs& a, uint16_t* sKV) {
+  constexpr int NW = 8, BQ = NW * QB * 32;
   static_assert(NW * 6 == kTileFrags && BQ % BK == 0, "tile shape");
-  __shared__ __attribute__((aligned(16))) uint16_t sKV[2 * kTileElems];
   TileIter ti;
   if (!tile_iter<SPARSE>(a, ti)) return;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  if (static_bound_holds(a, lane)) return;          // the static kernel handles these weights
-  const int N = a.g.N, rb = (wave * QB * 32) / BK, nt = ti.ntiles;
+  if (static_bound_holds(a, lane) != (MODE == kStatic)) return;   // the other kernel handles these weights
+  const int N = a.g.N, nt = ti.ntiles;
+  int rbit[QB];
+#pragma unroll
+  for (int qb = 0; qb < QB; ++qb) rbit[qb] = router_block<QB, SPARSE>(wave, qb);
   const uint16_t* img = a.kvf + (size_t)ti.head * a.nb * kTileElems;
   if (nt > 0) dma_tile(img + (size_t)ti.tile(0, SPARSE) * kTileElems, wave, lane, sKV);
   bf16x8 qf[QB][6];
-  load_q<QB, BQ>(a, ti.head, ti.qt, wave, lane, qf);
+  load_q<QB, BQ, SPARSE>(a, ti.head, ti.qt, wave, lane, qf);
   f32x16 acc[QB][3];
   float m[QB], l[QB];
+  int pad[QB];                                     // static mode: keys past the grid counted in l
 #pragma unroll
   for (int qb = 0; qb < QB; ++qb) {
     m[qb] = -1e30f;
     l[qb] = 0.f;
+    pad[qb] = 0;
 #pragma unroll
     for (int db = 0; db < 3; ++db) acc[qb][db] = f32x16{};
   }
@@ -457,71 +511,46 @@ __global__ void __launch_bounds__(512) attn_online_kernel(AttnArgs a) {
     const int st = it & 1, tile = ti.tile(it, SPARSE);
     if (it + 1 < nt)
       dma_tile(img + (size_t)ti.tile(it + 1, SPARSE) * kTileElems, wave, lane, sKV + (st ^ 1) * kTileElems);
-    if ((ti.flags(it, SPARSE) >> rb) & 1) {
-      const uint16_t* T_ = sKV + st * kTileElems;
-      const bool ragged = (tile + 1) * BK > N;
-#pragma unroll 1
-      for (int kb = 0; kb < SUB; ++kb) {
-        f32x16 S[QB];
-        qk_block<QB>(T_, kb, lane, qf, S);
-        bf16x8 P[QB][2];
-        softmax_online<QB>(S, ragged, tile * BK + kb * 32, N, lane, m, l, acc, P);
-        pv_block<QB>(T_, kb, lane, P, acc);
-      }
+    const int flags = ti.flags(it, SPARSE);
+    int qm = 0;
+#pragma unroll
+    for (int qb = 0; qb < QB; ++qb) qm |= ((flags >> rbit[qb]) & 1) << qb;
+    const uint16_t* T_ = sKV + st * kTileElems;
+    const bool ragged = (tile + 1) * BK > N;
+    if constexpr (SPARSE && QB == 2) {
+      if (qm == 3)
+        tile_body<QB, 3, MODE>(T_, lane, qf, acc, m, l, ragged, tile * BK, N);
+      else if (qm == 1)
+        tile_body<QB, 1, MODE>(T_, lane, qf, acc, m, l, ragged, tile * BK, N);
+      else if (qm == 2)
+        tile_body<QB, 2, MODE>(T_, lane, qf, acc, m, l, ragged, tile * BK, N);
+    } else {
+      tile_body<QB, (1 << QB) - 1, MODE>(T_, lane, qf, acc, m, l, ragged, tile * BK, N);
+    }
+    if constexpr (MODE == kStatic) {
+#pragma unroll
+      for (int qb = 0; qb < QB; ++qb) pad[qb] += ((qm >> qb) & 1) ? max(0, (tile + 1) * BK - N) : 0;
     }
     tile_barrier();
   }
-  store_o<QB>(a, ti.head, ti.qt * BQ + wave * QB * 32, lane, acc, l);
+  if constexpr (MODE == kStatic) {
+    // Padded keys sit in both lane halves; the row sum over both halves drops them exactly.
+#pragma unroll
+    for (int qb = 0; qb < QB; ++qb) l[qb] -= (lane < 32) ? (float)pad[qb] : 0.f;
+  }
+  store_o<QB, BQ, SPARSE>(a, ti.head, ti.qt, wave, lane, acc, l);
 }
 
-// Static-softmax kernel.  Keys past the grid have zero K^ and V: S = 0 and p = 1 there, they add nothing to
-// O and their count is taken off the row sum at the end -- no masking inside the loop.
 template <int QB, bool SPARSE>
 __global__ void __launch_bounds__(512) attn_static_kernel(AttnArgs a) {
-  constexpr int NW = 8, BQ = NW * QB * 32, SUB = BK / 32;
-  static_assert(NW * 6 == kTileFrags && BQ % BK == 0, "tile shape");
   __shared__ __attribute__((aligned(16))) uint16_t sKV[2 * kTileElems];
-  TileIter ti;
-  if (!tile_iter<SPARSE>(a, ti)) return;
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  if (!static_bound_holds(a, lane)) return;         // the online kernel handles these weights
-  const int N = a.g.N, rb = (wave * QB * 32) / BK, nt = ti.ntiles;
-  const uint16_t* img = a.kvf + (size_t)ti.head * a.nb * kTileElems;
-  if (nt > 0) dma_tile(img + (size_t)ti.tile(0, SPARSE) * kTileElems, wave, lane, sKV);
-  bf16x8 qf[QB][6];
-  load_q<QB, BQ>(a, ti.head, ti.qt, wave, lane, qf);
-  f32x16 acc[QB][3];
-  float l[QB];
-#pragma unroll
-  for (int qb = 0; qb < QB; ++qb) {
-    l[qb] = 0.f;
-#pragma unroll
-    for (int db = 0; db < 3; ++db) acc[qb][db] = f32x16{};
-  }
-  tile_barrier();
-  int pad = 0;                                      // keys past the grid counted in l
-  for (int it = 0; it < nt; ++it) {
-    const int st = it & 1, tile = ti.tile(it, SPARSE);
-    if (it + 1 < nt)
-      dma_tile(img + (size_t)ti.tile(it + 1, SPARSE) * kTileElems, wave, lane, sKV + (st ^ 1) * kTileElems);
-    if ((ti.flags(it, SPARSE) >> rb) & 1) {
-      const uint16_t* T_ = sKV + st * kTileElems;
-#pragma unroll 1
-      for (int kb = 0; kb < SUB; ++kb) {
-        f32x16 S[QB];
-        qk_block<QB>(T_, kb, lane, qf, S);
-        bf16x8 P[QB][2];
-        softmax_static<QB>(S, l, P);
-        pv_block<QB>(T_, kb, lane, P, acc);
-      }
-      pad += max(0, (tile + 1) * BK - N);
-    }
-    tile_barrier();
-  }
-  // Padded keys sit in both lane halves; the row sum over both halves drops them exactly.
-#pragma unroll
-  for (int qb = 0; qb < QB; ++qb) l[qb] -= (lane < 32) ? (float)pad : 0.f;
-  store_o<QB>(a, ti.head, ti.qt * BQ + wave * QB * 32, lane, acc, l);
+  attn_kernel_body<QB, SPARSE, kStatic>(a, sKV);
+}
+
+template <int QB, bool SPARSE>
+__global__ void __launch_bounds__(512) attn_online_kernel(AttnArgs a) {
+  __shared__ __attribute__((aligned(16))) uint16_t sKV[2 * kTileElems];
+  attn_kernel_body<QB, SPARSE, kOnline>(a, sKV);
 }
 
 // Block-sparse iteration lists: for each (head, query tile) the ascending KV blocks kept by any of the
