@@ -23,6 +23,11 @@ hidden 5376, 3D multimodal RoPE):
 5. block-sparse: keys outside the kept 128-token KV blocks of the query's
    block are excluded and the softmax renormalises over the kept keys; a
    query block with no kept block gets O = 0.
+6. joint attention (``attention_joint``): queries and keys are separate token
+   sets, each token with an explicit integer (t, h, w) position -- the
+   single-stream DiT with 3D multimodal RoPE over text, reference-image and
+   target tokens (H3-Image spec table, "DiT" and reference-image rows).
+   Steps 2-4 are unchanged; only the positions come from the caller.
 
 Everything is float64 on the exact input values.  BLAS matmuls serve as steps;
 there is no blocking or online softmax here.
@@ -137,4 +142,34 @@ def attention(Q, K, V, wq, wk, T, H, W, theta=1e4, eps=1e-6, heads=None, rows=No
             allowed = None if mask is None else _allowed(np.asarray(mask[hd]), rr, N, block)
             P = softmax_rows(L, allowed)
             out[r0:r0 + chunk, hi, :] = P @ vh
+    return out
+
+
+def prepare_at(x, w, pos, theta, eps) -> np.ndarray:
+    """RMSNorm then 3D RoPE of x [rows, 96] (one head) at explicit positions pos [rows, 3]."""
+    pos = np.asarray(pos, dtype=np.int64)
+    return rope_3d(rms_norm(x, w, eps), pos[:, 0], pos[:, 1], pos[:, 2], theta)
+
+
+def attention_joint(Q, K, V, wq, wk, q_pos, k_pos, theta=1e4, eps=1e-6, heads=None, rows=None,
+                    chunk=256) -> np.ndarray:
+    """Joint attention: O for the selected query rows and heads, float64 [len(rows), len(heads), 96].
+
+    Q is indexable as [Nq, heads, 96] at q_pos [Nq, 3]; K, V as [Nkv, heads, 96] at k_pos [Nkv, 3].
+    Every query attends to every key (non-causal), softmax scale 1/sqrt(96).
+    """
+    Nq = Q.shape[0]
+    nheads = Q.shape[1]
+    q_pos = np.asarray(q_pos)
+    k_pos = np.asarray(k_pos)
+    heads = list(range(nheads)) if heads is None else list(heads)
+    rows = np.arange(Nq) if rows is None else np.asarray(rows, dtype=np.int64)
+    out = np.zeros((len(rows), len(heads), D), dtype=np.float64)
+    for hi, hd in enumerate(heads):
+        kh = prepare_at(_head_slice(K, None, hd), wk, k_pos, theta, eps)
+        vh = _head_slice(V, None, hd)
+        for r0 in range(0, len(rows), chunk):
+            rr = rows[r0:r0 + chunk]
+            qh = prepare_at(_head_slice(Q, rr, hd), wq, q_pos[rr], theta, eps)
+            out[r0:r0 + chunk, hi, :] = softmax_rows(qh @ kh.T / math.sqrt(D)) @ vh
     return out

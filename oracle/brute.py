@@ -49,3 +49,26 @@ def attention(Q, K, V, wq, wk, T, H, W, theta=1e4, eps=1e-6, mask=None, block=12
             for c in range(d):
                 out[i][hd][c] = sum(ex[a] * float(V[j][hd][c]) for a, j in enumerate(keys)) / tot
     return out
+
+
+def attention_joint(Q, K, V, wq, wk, q_pos, k_pos, theta=1e4, eps=1e-6):
+    """Joint attention with explicit positions, as nested lists: Q [Nq][heads][96] at q_pos [Nq][3],
+    K, V [Nkv][heads][96] at k_pos [Nkv][3]; every query sees every key."""
+    heads = len(Q[0])
+    d = len(Q[0][0])
+    wq = [float(x) for x in wq]
+    wk = [float(x) for x in wk]
+    out = [[[0.0] * d for _ in range(heads)] for _ in range(len(Q))]
+    for hd in range(heads):
+        qs = [_normalise_rotate([float(x) for x in Q[i][hd]], wq, *[int(p) for p in q_pos[i]], theta, eps)
+              for i in range(len(Q))]
+        ks = [_normalise_rotate([float(x) for x in K[j][hd]], wk, *[int(p) for p in k_pos[j]], theta, eps)
+              for j in range(len(K))]
+        for i in range(len(Q)):
+            lg = [sum(qs[i][c] * ks[j][c] for c in range(d)) / math.sqrt(d) for j in range(len(K))]
+            top = max(lg)
+            ex = [math.exp(x - top) for x in lg]
+            tot = sum(ex)
+            for c in range(d):
+                out[i][hd][c] = sum(ex[j] * float(V[j][hd][c]) for j in range(len(K))) / tot
+    return out

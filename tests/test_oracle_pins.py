@@ -14,7 +14,7 @@ import pytest
 from oracle import attention as A
 from oracle import brute as B
 from oracle import router as R
-from synth import custom_workload, make_inputs
+from synth import custom_workload, make_inputs, make_joint_inputs
 
 GOLD = os.path.join(os.path.dirname(__file__), "golden")
 rng0 = np.random.default_rng(1234)
@@ -332,3 +332,59 @@ def test_router_fp32_mask_differs_from_exact_only_at_near_ties():
             row = np.sort(ex[i][np.isfinite(ex[i])])[::-1]
             gap = row[keep - 2] - row[keep - 1]
             assert gap <= 1e-5 * np.max(np.abs(row))
+
+
+# ------------------------------------------------------------------------------------ joint attention
+def test_joint_with_grid_positions_equals_grid_oracle():
+    """Joint attention whose tokens sit at their grid positions is the grid layer itself."""
+    x = make_inputs("s1")
+    wl = x.workload
+    pos = np.stack(A.positions(wl.T, wl.H, wl.W), axis=1)
+    got = A.attention_joint(x.q, x.k, x.v, x.wq, x.wk, pos, pos, wl.theta, wl.eps)
+    ref = A.attention(x.q, x.k, x.v, x.wq, x.wk, wl.T, wl.H, wl.W, wl.theta, wl.eps)
+    assert np.max(np.abs(got - ref)) <= 1e-13
+
+
+def test_joint_shift_of_all_positions_changes_nothing():
+    """RoPE rotations compose: shifting every query and key coordinate by the same per-axis offset
+    leaves all logits, hence O, unchanged."""
+    x = make_joint_inputs("j_small")
+    wl = x.workload
+    rows = np.arange(0, wl.Nq, 37)
+    ref = A.attention_joint(x.q, x.k, x.v, x.wq, x.wk, x.q_pos, x.k_pos, wl.theta, wl.eps, rows=rows)
+    off = np.array([7, 3, 11])
+    got = A.attention_joint(x.q, x.k, x.v, x.wq, x.wk, x.q_pos + off, x.k_pos + off, wl.theta, wl.eps,
+                            rows=rows)
+    assert np.max(np.abs(got - ref)) <= 1e-12
+    # a shift of the keys alone does change the result (positions do enter)
+    moved = A.attention_joint(x.q, x.k, x.v, x.wq, x.wk, x.q_pos, x.k_pos + off, wl.theta, wl.eps, rows=rows)
+    assert np.max(np.abs(moved - ref)) > 1e-3
+
+
+def test_joint_brute_force_tiny():
+    x = make_joint_inputs("j_tiny")
+    wl = x.workload
+    q, k, v = np.asarray(x.q, np.float64), np.asarray(x.k, np.float64), np.asarray(x.v, np.float64)
+    ref = np.array(B.attention_joint(q.tolist(), k.tolist(), v.tolist(), x.wq, x.wk, x.q_pos.tolist(),
+                                         x.k_pos.tolist(), wl.theta, wl.eps))
+    got = A.attention_joint(x.q, x.k, x.v, x.wq, x.wk, x.q_pos, x.k_pos, wl.theta, wl.eps)
+    assert np.max(np.abs(got - ref)) <= 1e-12
+
+
+def test_joint_brute_force_queries_shorter_than_keys():
+    x = make_joint_inputs("j_small")
+    wl = x.workload
+    qi = np.array([0, 1, 300, wl.Nq - 1])          # a few queries against all 1314 keys, one head
+    q = np.asarray(x.q, np.float64)[qi][:, :1]
+    k, v = np.asarray(x.k, np.float64)[:, :1], np.asarray(x.v, np.float64)[:, :1]
+    ref = np.array(B.attention_joint(q.tolist(), k.tolist(), v.tolist(), x.wq, x.wk, x.q_pos[qi].tolist(),
+                                         x.k_pos.tolist(), wl.theta, wl.eps))
+    got = A.attention_joint(x.q, x.k, x.v, x.wq, x.wk, x.q_pos, x.k_pos, wl.theta, wl.eps, heads=[0], rows=qi)
+    assert np.max(np.abs(got - ref)) <= 1e-12
+
+
+def test_joint_single_key_gives_v():
+    x = make_joint_inputs("j_tiny")
+    wl = x.workload
+    got = A.attention_joint(x.q, x.k[3:4], x.v[3:4], x.wq, x.wk, x.q_pos, x.k_pos[3:4], wl.theta, wl.eps)
+    assert np.array_equal(got, np.broadcast_to(np.asarray(x.v[3:4], np.float64), got.shape))
