@@ -32,6 +32,8 @@ DESCR = {
     "v5s": "route + block-sparse attention (sparsity 0.75, 128-token blocks), 124,992 tokens, 56 heads x 96",
     "v10s": "route + block-sparse attention (sparsity 0.80, 128-token blocks), 245,952 tokens, 56 heads x 96",
     "v10d": "dense attention, 10 s video token grid 61x48x84 = 245,952 tokens, 56 heads x 96",
+    "j_edit2": ("joint attention, image edit with 2 reference images: 65,536 target queries against "
+                "197,120 keys (512 text + 2 x 65,536 reference + 65,536 target tokens), 56 heads x 96"),
 }
 
 
@@ -64,6 +66,57 @@ def executed_flops(mask: np.ndarray, N: int, block: int = 128, d: int = 96) -> f
     return float(4.0 * d * per_head.sum())
 
 
+def bench_joint(args, torch, dit):
+    """Joint attention (explicit positions, queries = target tokens, keys = the whole sequence)."""
+    from synth import make_joint_inputs
+    x = make_joint_inputs(args.workload)
+    wl = x.workload
+    dev = torch.device("cuda:0")
+
+    def up(b):
+        return torch.from_numpy(b.bits.view(np.int16)).to(dev).view(torch.bfloat16)
+
+    q, k, v = up(x.q), up(x.k), up(x.v)
+    wq, wk = torch.from_numpy(x.wq).to(dev), torch.from_numpy(x.wk).to(dev)
+    qp = torch.from_numpy(x.q_pos).to(dev)
+    kp = torch.from_numpy(x.k_pos).to(dev)
+    o = torch.empty_like(q)
+    ws = torch.empty(dit.dit_attn_joint_workspace_bytes(wl.Nq, wl.Nkv, wl.heads, 96, x.max_pos), dtype=torch.uint8,
+                     device=dev)
+    stream = torch.cuda.current_stream()
+
+    def call():
+        dit.dit_attn_joint(q, k, v, wq, wk, qp, kp, x.max_pos, wl.theta, wl.eps, o=o, workspace=ws)
+
+    for _ in range(args.warmup):
+        call()
+    torch.cuda.synchronize()
+    events = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(args.steps)]
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        events[i][0].record(stream)
+        call()
+        events[i][1].record(stream)
+    torch.cuda.synchronize()
+    ms_step = (time.perf_counter() - t0) * 1e3 / args.steps
+    ms_call = float(np.mean([e[0].elapsed_time(e[1]) for e in events]))
+    flops = 4.0 * wl.Nq * wl.Nkv * 96 * wl.heads
+    tflops = flops / (ms_step * 1e-3) / 1e12
+    result = {
+        "metric": METRIC, "value": round(tflops, 2), "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": round(ms_step, 3), "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "bf16", "data": "synthetic (seeded N(0,1) bf16 Q/K/V; norm weights 1+0.1N(0,1))",
+        "config": {"workload": f"{wl.name}: {DESCR[wl.name]}", "queries": wl.Nq, "keys": wl.Nkv, "heads": wl.heads,
+                   "head_dim": 96, "mode": "joint"},
+        "frac_of_bf16_peak": round(tflops / PEAK_BF16_TFLOPS, 4),
+        "roofline": {"bound": "mfma", "achieved": round(flops / (ms_call * 1e-3) / 1e12, 2), "peak": PEAK_BF16_TFLOPS,
+                     "unit": "TFLOP/s", "frac": round(flops / (ms_call * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4),
+                     "traffic": None, "kernel": "attn_static_kernel<2, false>", "kernel_ms": round(ms_call, 3),
+                     "timed": "whole call: K^/V fragment prepass + attention kernels", "flops_per_launch": flops},
+    }
+    print(json.dumps(result), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -84,6 +137,9 @@ def main():
     import torch
     import image_diffusion_transformer_amd as dit
     from synth import WORKLOADS, make_inputs
+
+    if args.workload.startswith("j_"):
+        return bench_joint(args, torch, dit)
 
     wl = WORKLOADS[args.workload]
     dev = torch.device("cuda:0")

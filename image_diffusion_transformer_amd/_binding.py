@@ -22,7 +22,7 @@ STATUS_NAMES = {0: "DIT_OK", 1: "DIT_ERR_INVALID_ARG", 2: "DIT_ERR_UNSUPPORTED",
                 3: "DIT_ERR_WORKSPACE", 4: "DIT_ERR_HIP"}
 
 EXPORTS = ("dit_attn_workspace_bytes", "dit_attn_keep_count", "dit_attn_dense", "dit_attn_route",
-           "dit_attn_block_sparse", "dit_attn_last_error")
+           "dit_attn_block_sparse", "dit_attn_joint_workspace_bytes", "dit_attn_joint", "dit_attn_last_error")
 
 _lib = None
 _lock = threading.Lock()
@@ -54,6 +54,10 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
         lib.dit_attn_route.restype = i
         lib.dit_attn_block_sparse.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, i, f, f, i, vp, vp, vp, sz, vp]
         lib.dit_attn_block_sparse.restype = i
+        lib.dit_attn_joint_workspace_bytes.argtypes = [i, i, i, i, i]
+        lib.dit_attn_joint_workspace_bytes.restype = sz
+        lib.dit_attn_joint.argtypes = [vp, vp, vp, vp, vp, vp, vp, i, i, i, i, i, f, f, vp, vp, sz, vp]
+        lib.dit_attn_joint.restype = i
         lib.dit_attn_last_error.argtypes = []
         lib.dit_attn_last_error.restype = ctypes.c_char_p
         _lib = lib
@@ -138,6 +142,35 @@ def dit_attn_block_sparse(q, k, v, wq, wk, grid, mask, rope_theta=10000.0, eps=1
     _check(load_library().dit_attn_block_sparse(_ptr(q), _ptr(k), _ptr(v), _ptr(wq), _ptr(wk), T, H, W, heads, d,
                                                  rope_theta, eps, block, _ptr(mask), _ptr(o), _ptr(workspace),
                                                  workspace.numel(), _stream(stream)))
+    return o
+
+
+def dit_attn_joint_workspace_bytes(nq: int, nk: int, heads: int, head_dim: int = HEAD_DIM, max_pos: int = 1) -> int:
+    return int(load_library().dit_attn_joint_workspace_bytes(nq, nk, heads, head_dim, max_pos))
+
+
+def dit_attn_joint(q, k, v, wq, wk, q_pos, k_pos, max_pos, rope_theta=10000.0, eps=1e-6, o=None, workspace=None,
+                   stream=None):
+    """Joint attention: q bf16 [nq, heads, 96] at q_pos int32 [nq, 3], k / v bf16 [nk, heads, 96] at k_pos
+    int32 [nk, 3] (t, h, w positions, each coordinate < max_pos); writes o [nq, heads, 96]."""
+    if q.dim() != 3 or k.dim() != 3:
+        raise ValueError("q and k must be [tokens, heads, head_dim]")
+    nq, heads, d = (int(x) for x in q.shape)
+    nk = int(k.shape[0])
+    if tuple(q_pos.shape) != (nq, 3) or tuple(k_pos.shape) != (nk, 3):
+        raise ValueError("q_pos must be [nq, 3] and k_pos [nk, 3]")
+    if q_pos.dtype != torch.int32 or k_pos.dtype != torch.int32:
+        raise ValueError("positions must be int32")
+    if o is None:
+        o = torch.empty_like(q)
+    if workspace is None:
+        n = dit_attn_joint_workspace_bytes(nq, nk, heads, d, int(max_pos))
+        if n == 0:
+            raise DitAttnError(DIT_ERR_INVALID_ARG, "invalid sizes for joint workspace sizing")
+        workspace = torch.empty(n, dtype=torch.uint8, device=q.device)
+    _check(load_library().dit_attn_joint(_ptr(q), _ptr(k), _ptr(v), _ptr(wq), _ptr(wk), _ptr(q_pos), _ptr(k_pos),
+                                          nq, nk, heads, d, int(max_pos), rope_theta, eps, _ptr(o), _ptr(workspace),
+                                          workspace.numel(), _stream(stream)))
     return o
 
 

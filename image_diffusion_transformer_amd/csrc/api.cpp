@@ -170,6 +170,11 @@ dit::AttnArgs attn_args(const Shape& s, const void* q, const void* k, const void
   a.kvf = (uint16_t*)((char*)ws + L.kvf);
   a.o = (uint16_t*)o;
   a.g = grid_desc(s);
+  a.nq = (int)s.N;
+  a.nk = (int)s.N;
+  a.q_pos = nullptr;
+  a.k_pos = nullptr;
+  a.max_pos = 0;
   a.qscale = (float)(1.4426950408889634 / std::sqrt((double)dit::kHeadDim));
   a.eps = eps;
   a.nqt = s.nqt;
@@ -182,6 +187,48 @@ dit::AttnArgs attn_args(const Shape& s, const void* q, const void* k, const void
 int keep_count(int nb, float sparsity) {
   const double k = (double)nb - std::floor((double)sparsity * nb + 1e-9);
   return (int)std::max(1.0, std::min((double)nb, k));
+}
+
+// Joint attention: queries and keys are separate token sets with explicit positions.
+constexpr int kMaxPos = 1 << 20;
+
+struct JointShape {
+  int nq, nk, heads, nb, nqt, max_pos;
+};
+
+struct JointLayout {
+  size_t tab;   // RoPE table [max_pos][32] f32
+  size_t kvf;   // K^ / V^T fragment images [heads][nb] x 48 KB
+  size_t total;
+};
+
+JointLayout make_joint_layout(const JointShape& j) {
+  JointLayout L{};
+  L.tab = 0;
+  L.kvf = align256((size_t)j.max_pos * dit::kRopeRow * sizeof(float));
+  L.total = L.kvf + (size_t)j.heads * j.nb * dit::kTileImageBytes;
+  return L;
+}
+
+dit_status check_joint_shape(int nq, int nk, int heads, int head_dim, int max_pos, JointShape& j) {
+  if (nq < 1 || nk < 1 || heads < 1)
+    return fail(DIT_ERR_INVALID_ARG, "token counts and heads must be >= 1 (nq=%d nk=%d heads=%d)", nq, nk, heads);
+  if (head_dim != dit::kHeadDim)
+    return fail(DIT_ERR_UNSUPPORTED, "head_dim %d is not supported (only 96)", head_dim);
+  if (max_pos < 1) return fail(DIT_ERR_INVALID_ARG, "max_pos must be >= 1 (got %d)", max_pos);
+  if (max_pos > kMaxPos) return fail(DIT_ERR_UNSUPPORTED, "max_pos %d exceeds %d", max_pos, kMaxPos);
+  const long long big = std::max(nq, nk);
+  if (big * heads * dit::kHeadDim > 2147483647ll)
+    return fail(DIT_ERR_UNSUPPORTED, "tokens*heads*head_dim = %lld exceeds 2^31-1 elements",
+                big * heads * dit::kHeadDim);
+  j.nq = nq;
+  j.nk = nk;
+  j.heads = heads;
+  j.nb = (nk + dit::kBlock - 1) / dit::kBlock;
+  const int bq = dit::attn_query_tile();
+  j.nqt = (nq + bq - 1) / bq;
+  j.max_pos = max_pos;
+  return DIT_OK;
 }
 
 }  // namespace
@@ -287,6 +334,66 @@ dit_status dit_attn_block_sparse(const void* q, const void* k, const void* v, co
   a.list_len = c.list_len;
   e = dit::launch_attn_sparse(a, stream);
   if (e != hipSuccess) return fail_hip(e, "sparse attention kernel launch");
+  return DIT_OK;
+}
+
+size_t dit_attn_joint_workspace_bytes(int nq, int nk, int heads, int head_dim, int max_pos) {
+  JointShape j;
+  std::string saved = g_err;
+  const dit_status st = check_joint_shape(nq, nk, heads, head_dim, max_pos, j);
+  g_err = saved;
+  if (st != DIT_OK) return 0;
+  return make_joint_layout(j).total;
+}
+
+dit_status dit_attn_joint(const void* q, const void* k, const void* v, const float* wq, const float* wk,
+                          const int* q_pos, const int* k_pos, int nq, int nk, int heads, int head_dim, int max_pos,
+                          float rope_theta, float eps, void* o, void* workspace, size_t workspace_bytes,
+                          void* hip_stream) {
+  g_err.clear();
+  JointShape j;
+  dit_status st = check_joint_shape(nq, nk, heads, head_dim, max_pos, j);
+  if (st != DIT_OK) return st;
+  if ((st = check_common(q, k, wq, wk, rope_theta, eps)) != DIT_OK) return st;
+  if (!v || !o || !q_pos || !k_pos) return fail(DIT_ERR_INVALID_ARG, "null v, o, q_pos or k_pos");
+  if (!aligned16(v) || !aligned16(o)) return fail(DIT_ERR_INVALID_ARG, "v and o must be 16-byte aligned");
+  if (((uintptr_t)q_pos & 3u) || ((uintptr_t)k_pos & 3u))
+    return fail(DIT_ERR_INVALID_ARG, "q_pos and k_pos must be 4-byte aligned");
+  const JointLayout L = make_joint_layout(j);
+  if (!workspace) return fail(DIT_ERR_WORKSPACE, "workspace is null (need %zu bytes)", L.total);
+  if (workspace_bytes < L.total)
+    return fail(DIT_ERR_WORKSPACE, "workspace has %zu bytes, need %zu", workspace_bytes, L.total);
+  if (((uintptr_t)workspace & 255u) != 0) return fail(DIT_ERR_INVALID_ARG, "workspace must be 256-byte aligned");
+  hipStream_t stream = (hipStream_t)hip_stream;
+  // rows p = 0 .. max_pos-1: cos / sin of p * theta^(-2i/32), the same for the three axes
+  const std::vector<float>& tab = rope_table(max_pos, 0, 0, rope_theta);
+  hipError_t e = hipMemcpyAsync((char*)workspace + L.tab, tab.data(), tab.size() * sizeof(float),
+                                hipMemcpyHostToDevice, stream);
+  if (e != hipSuccess) return fail_hip(e, "hipMemcpyAsync(rope table)");
+  dit::AttnArgs a{};
+  a.q = (const uint16_t*)q;
+  a.k = (const uint16_t*)k;
+  a.v = (const uint16_t*)v;
+  a.wq = wq;
+  a.wk = wk;
+  a.rope = (const float*)((const char*)workspace + L.tab);
+  a.kvf = (uint16_t*)((char*)workspace + L.kvf);
+  a.o = (uint16_t*)o;
+  a.g = dit::GridDesc{};
+  a.g.heads = heads;
+  a.nq = nq;
+  a.nk = nk;
+  a.q_pos = q_pos;
+  a.k_pos = k_pos;
+  a.max_pos = max_pos;
+  a.qscale = (float)(1.4426950408889634 / std::sqrt((double)dit::kHeadDim));
+  a.eps = eps;
+  a.nqt = j.nqt;
+  a.total = heads * j.nqt;
+  a.per_xcd = (a.total + 7) / 8;
+  a.nb = j.nb;
+  e = dit::launch_attn_dense(a, stream);
+  if (e != hipSuccess) return fail_hip(e, "joint attention kernel launch");
   return DIT_OK;
 }
 

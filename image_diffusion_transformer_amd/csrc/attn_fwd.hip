@@ -109,8 +109,21 @@ __device__ __forceinline__ float pair_sum(float x) {
   return __uint_as_float(r[0]) + __uint_as_float(r[1]);
 }
 
-__device__ __forceinline__ int rope_row(const GridDesc& g, int axis, int t, int h, int w) {
-  return axis == 0 ? t : (axis == 1 ? g.T + h : g.T + g.H + w);
+// Rows of the RoPE table that rotate the three axis chunks of token n.  Grid tokens: rows t, T + h and
+// T + H + w of the per-axis table.  Tokens with explicit (t, h, w) positions: the coordinates themselves,
+// in one table of max_pos rows that serves all three axes (its rows depend only on the position);
+// coordinates outside [0, max_pos) are clamped to it.
+__device__ __forceinline__ void rope_rows(const AttnArgs& a, const int* pos, int n, int (&r)[3]) {
+  if (pos != nullptr) {
+#pragma unroll
+    for (int i = 0; i < 3; ++i) r[i] = min(max(pos[3 * (size_t)n + i], 0), a.max_pos - 1);
+  } else {
+    int t, h, w;
+    grid_pos((uint32_t)n, a.g, t, h, w);
+    r[0] = t;
+    r[1] = a.g.T + h;
+    r[2] = a.g.T + a.g.H + w;
+  }
 }
 
 // RMS-normalise (scale r) and rotate 8 consecutive channels 8c..8c+7 held as bf16 in `raw`.
@@ -183,7 +196,7 @@ __device__ __forceinline__ void load_q(const AttnArgs& a, int head, int qt, int 
 #pragma unroll
   for (int qb = 0; qb < QB; ++qb) {
     const int n = qt * BQ + query_block<QB, SPARSE>(wave, qb) * 32 + l32;
-    const bool live = n < a.g.N;
+    const bool live = n < a.nq;
     u32x4 raw[6];
     const size_t base = ((size_t)(live ? n : 0) * a.g.heads + head) * kHeadDim;
 #pragma unroll
@@ -199,12 +212,12 @@ __device__ __forceinline__ void load_q(const AttnArgs& a, int head, int qt, int 
       }
     ss = pair_sum(ss);
     const float r = live ? __builtin_amdgcn_rsqf(ss * (1.0f / kHeadDim) + a.eps) : 0.f;
-    int t = 0, h = 0, w = 0;
-    if (live) grid_pos((uint32_t)n, a.g, t, h, w);
+    int rr[3] = {0, 0, 0};
+    if (live) rope_rows(a, a.q_pos, n, rr);
 #pragma unroll
     for (int ks = 0; ks < 6; ++ks) {
       const int c = 2 * ks + half;
-      const float* rp = a.rope + rope_row(a.g, ks >> 1, t, h, w) * kRopeRow;
+      const float* rp = a.rope + rr[ks >> 1] * kRopeRow;
       qf[qb][ks] = __builtin_bit_cast(bf16x8, norm_rope_chunk(raw[ks], r, a.qscale, rp, c, a.wq));
     }
   }
@@ -323,7 +336,7 @@ __device__ __forceinline__ void store_o(const AttnArgs& a, int head, int qt, int
     const int n = qt * BQ + query_block<QB, SPARSE>(wave, qb) * 32 + l32;
     const float lt = pair_sum(l[qb]);
     const float inv = lt > 0.f ? 1.0f / lt : 0.f;
-    if (n < a.g.N) {
+    if (n < a.nq) {
       uint16_t* op = a.o + ((size_t)n * a.g.heads + head) * kHeadDim;
 #pragma unroll
       for (int db = 0; db < 3; ++db)
@@ -357,7 +370,7 @@ __device__ __forceinline__ bool tile_iter(const AttnArgs& a, TileIter& ti) {
     ti.ntiles = a.list_len[logical];
     ti.lst = a.list + (size_t)logical * a.nb;
   } else {
-    ti.ntiles = (a.g.N + BK - 1) / BK;
+    ti.ntiles = (a.nk + BK - 1) / BK;
     ti.lst = nullptr;
   }
   return true;
@@ -372,7 +385,7 @@ __global__ void __launch_bounds__(256) kv_prep_kernel(AttnArgs a) {
   __shared__ __attribute__((aligned(16))) uint16_t rv[BK * kHeadDim];
   __shared__ __attribute__((aligned(16))) float sW[kHeadDim];
   const int tile = blockIdx.x, head = blockIdx.y, tid = threadIdx.x;
-  const int N = a.g.N;
+  const int N = a.nk;
   if (tid < kHeadDim) sW[tid] = a.wk[tid];
   for (int i = tid; i < BK * 12; i += 256) {
     const int row = i / 12, c = i - 12 * row;
@@ -404,12 +417,12 @@ __global__ void __launch_bounds__(256) kv_prep_kernel(AttnArgs a) {
       }
     }
     const float r = live ? __builtin_amdgcn_rsqf(ss * (1.0f / kHeadDim) + a.eps) : 0.f;
-    int t = 0, h = 0, w = 0;
-    if (live) grid_pos((uint32_t)n, a.g, t, h, w);
+    int rr[3] = {0, 0, 0};
+    if (live) rope_rows(a, a.k_pos, n, rr);
 #pragma unroll
     for (int j = 0; j < 6; ++j) {
       const int c = 6 * cg + j;                        // channels 8c .. 8c+7 = step c/2, lane half c%2
-      const float* rp = a.rope + rope_row(a.g, c >> 2, t, h, w) * kRopeRow;
+      const float* rp = a.rope + rr[c >> 2] * kRopeRow;
       const u32x4 y = norm_rope_chunk(row[c], r, 1.0f, rp, c, sW);
       *(u32x4*)(img + ((kk >> 5) * 6 + (c >> 1)) * kFrag + ((c & 1) * 32 + (kk & 31)) * 8) =
           live ? y : u32x4{0, 0, 0, 0};
@@ -487,7 +500,7 @@ __device__ __forceinline__ void attn_kernel_body(const AttnArgs& a, uint16_t* sK
   if (!tile_iter<SPARSE>(a, ti)) return;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   if (static_bound_holds(a, lane) != (MODE == kStatic)) return;   // the other kernel handles these weights
-  const int N = a.g.N, nt = ti.ntiles;
+  const int N = a.nk, nt = ti.ntiles;
   int rbit[QB];
 #pragma unroll
   for (int qb = 0; qb < QB; ++qb) rbit[qb] = router_block<QB, SPARSE>(wave, qb);

@@ -44,7 +44,11 @@ struct AttnArgs {
   const float* rope;      // [(T+H+W)][32]: row t, then T+h, then T+H+w; cos[16], sin[16]
   uint16_t* kvf;          // [heads][nb][48][512] bf16: K^ / V^T MFMA fragment image per 128-key tile
   uint16_t* o;
-  GridDesc g;
+  GridDesc g;             // token grid (grid calls); heads is used by every call
+  int nq, nk;             // query and key token counts (both N for grid calls)
+  const int* q_pos;       // null for grid calls; else int32 [nq][3] (t, h, w) explicit positions
+  const int* k_pos;       // null for grid calls; else int32 [nk][3]
+  int max_pos;            // explicit positions: rows of the shared RoPE table (coordinates are clamped)
   float qscale;           // log2(e) / sqrt(96): softmax runs in base 2
   float eps;
   int nqt;                // query tiles per head
@@ -53,7 +57,7 @@ struct AttnArgs {
   // block-sparse iteration lists (null for dense)
   const int* list;        // [heads][nqt][nb]: kv block | (router-block flags << 24)
   const int* list_len;    // [heads][nqt]
-  int nb;
+  int nb;                 // 128-key tiles: ceil(nk / 128)
 };
 
 struct RouteArgs {

@@ -107,6 +107,32 @@ dit_status dit_attn_block_sparse(const void* q, const void* k, const void* v,
                                  void* o,
                                  void* workspace, size_t workspace_bytes, void* hip_stream);
 
+/* Bytes of device workspace dit_attn_joint needs for these sizes (0 if they are invalid). */
+size_t dit_attn_joint_workspace_bytes(int nq, int nk, int heads, int head_dim, int max_pos);
+
+/* Joint attention over one token sequence with explicit 3D positions: the
+ * single-stream DiT of H3-Image (spec table, "DiT" row: 3D multimodal RoPE)
+ * attends over text, reference-image (up to 16, reference-image row) and
+ * target tokens together.
+ *  - q: bf16 [nq][heads][head_dim] at positions q_pos: int32 [nq][3] (t, h, w);
+ *    k, v: bf16 [nk][heads][head_dim] at positions k_pos: int32 [nk][3].
+ *    nq and nk may differ (e.g. only the target tokens as queries against the
+ *    whole sequence as keys).  All device memory, owned by the caller.
+ *  - Positions are integers in [0, max_pos): every coordinate rotates its axis
+ *    chunk by pos * rope_theta^(-2i/32), as in the grid calls.  Coordinates
+ *    outside that range are clamped to it (no error is raised on the device).
+ *  - RMSNorm, RoPE, softmax and the MFMA path are those of dit_attn_dense; every
+ *    query attends to every key.  Writes o [nq][heads][head_dim] bf16.
+ *  - With q = k = the grid tokens at their grid positions the result equals
+ *    dit_attn_dense bit for bit. */
+dit_status dit_attn_joint(const void* q, const void* k, const void* v,
+                          const float* wq, const float* wk,
+                          const int* q_pos, const int* k_pos,
+                          int nq, int nk, int heads, int head_dim, int max_pos,
+                          float rope_theta, float eps,
+                          void* o,
+                          void* workspace, size_t workspace_bytes, void* hip_stream);
+
 /* Text of the last error on the calling thread ("" if the last call succeeded).
  * Valid until the next call on the same thread. */
 const char* dit_attn_last_error(void);

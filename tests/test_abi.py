@@ -144,3 +144,41 @@ def test_missing_library_fails_loudly(tmp_path):
             B.load_library(str(tmp_path / "libditattn.so"))
     finally:
         B._lib = saved
+
+
+def _joint(lib, **kw):
+    a = dict(q=FAKE, k=FAKE, v=FAKE, wq=FAKE, wk=FAKE, qp=FAKE, kp=FAKE, nq=20, nk=50, heads=2, d=96, maxp=16,
+             theta=1e4, eps=1e-6, o=FAKE, ws=FAKE, wsb=1 << 30, stream=None)
+    a.update(kw)
+    return lib.dit_attn_joint(a["q"], a["k"], a["v"], a["wq"], a["wk"], a["qp"], a["kp"], a["nq"], a["nk"], a["heads"],
+                              a["d"], a["maxp"], a["theta"], a["eps"], a["o"], a["ws"], a["wsb"], a["stream"])
+
+
+@pytest.mark.parametrize("kw,status,text", [
+    (dict(qp=None), B.DIT_ERR_INVALID_ARG, "null"),
+    (dict(kp=None), B.DIT_ERR_INVALID_ARG, "null"),
+    (dict(v=None), B.DIT_ERR_INVALID_ARG, "null"),
+    (dict(q=None), B.DIT_ERR_INVALID_ARG, "null"),
+    (dict(qp=FAKE + 2), B.DIT_ERR_INVALID_ARG, "4-byte"),
+    (dict(v=FAKE + 8), B.DIT_ERR_INVALID_ARG, "aligned"),
+    (dict(nq=0), B.DIT_ERR_INVALID_ARG, "token counts"),
+    (dict(nk=-3), B.DIT_ERR_INVALID_ARG, "token counts"),
+    (dict(maxp=0), B.DIT_ERR_INVALID_ARG, "max_pos"),
+    (dict(maxp=(1 << 20) + 1), B.DIT_ERR_UNSUPPORTED, "max_pos"),
+    (dict(d=128), B.DIT_ERR_UNSUPPORTED, "head_dim"),
+    (dict(nk=30_000_000), B.DIT_ERR_UNSUPPORTED, "exceeds"),
+    (dict(theta=-1.0), B.DIT_ERR_INVALID_ARG, "rope_theta"),
+    (dict(ws=None), B.DIT_ERR_WORKSPACE, "workspace"),
+    (dict(wsb=64), B.DIT_ERR_WORKSPACE, "need"),
+    (dict(ws=FAKE + 128), B.DIT_ERR_INVALID_ARG, "256-byte"),
+])
+def test_joint_validation_errors(lib, kw, status, text):
+    assert _joint(lib, **kw) == status
+    assert text in B.dit_attn_last_error()
+
+
+def test_joint_workspace_bytes(lib):
+    n = dit.dit_attn_joint_workspace_bytes(65536, 197120, 56, 96, 515)
+    assert n >= 56 * 1540 * 48 * 1024 + 515 * 32 * 4          # fragment images of 1540 key tiles + table
+    assert dit.dit_attn_joint_workspace_bytes(10, 10, 2, 96, 0) == 0
+    assert dit.dit_attn_joint_workspace_bytes(10, 0, 2, 96, 4) == 0
