@@ -32,6 +32,8 @@ DESCR = {
     "v5s": "route + block-sparse attention (sparsity 0.75, 128-token blocks), 124,992 tokens, 56 heads x 96",
     "v10s": "route + block-sparse attention (sparsity 0.80, 128-token blocks), 245,952 tokens, 56 heads x 96",
     "v10d": "dense attention, 10 s video token grid 61x48x84 = 245,952 tokens, 56 heads x 96",
+    "v5h7": ("dense attention, 124,992 tokens, 7 heads x 96: one GPU's head share when the 56-head layer is "
+             "split by head over 8 GPUs"),
     "j_edit2": ("joint attention, image edit with 2 reference images: 65,536 target queries against "
                 "197,120 keys (512 text + 2 x 65,536 reference + 65,536 target tokens), 56 heads x 96"),
 }
@@ -126,7 +128,8 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--calib-copy", action="store_true",
                     help="also run one plain 1 GiB device copy (HBM counter calibration)")
-    ap.add_argument("--traffic", default=os.path.join(ROOT, "profiles", "traffic_dense_v5.json"))
+    ap.add_argument("--traffic", default=None,
+                    help="HBM counter summary for the attention kernel (default: profiles/traffic_<workload>.json)")
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -215,8 +218,9 @@ def main():
     attn_tflops = flops / (ms_attn * 1e-3) / 1e12
 
     traffic = None
-    if not sparse and os.path.exists(args.traffic):
-        with open(args.traffic) as f:
+    traffic_path = args.traffic or os.path.join(ROOT, "profiles", f"traffic_{wl.name}.json")
+    if os.path.exists(traffic_path):
+        with open(traffic_path) as f:
             tr = json.load(f)
         # counters taken on another version of the kernel source say nothing about this one
         if tr.get("workload") == wl.name and tr.get("source_sha256") == kernel_source_sha256():

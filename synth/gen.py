@@ -72,6 +72,9 @@ WORKLOADS = {
                  notes="10 s 1344x768 video token grid (245,952 tokens), sparsity 0.80"),
         Workload("v10d", 61, 48, 84, 56, seed=3, smooth=True,
                  notes="10 s video grid, dense"),
+        Workload("v5h7", 31, 48, 84, 7, seed=2, smooth=True,
+                 notes="5 s video grid with 7 heads: one GPU's share of the layer when its 56 heads are "
+                       "split over 8 GPUs (sequence-parallel attention resharded by head)"),
         # small grids for element-by-element parity: several tiles plus ragged tails
         Workload("s1", 2, 10, 10, 2, seed=10, smooth=True, notes="N=200 (tail 72)"),
         Workload("s2", 3, 16, 16, 3, seed=11, smooth=True, notes="N=768 (6 full blocks)"),
