@@ -45,8 +45,8 @@ struct Shape {
 struct Layout {
   size_t tab;        // RoPE table [(T+H+W)][32] f32
   size_t kvf;        // K^ / V^T fragment images [heads][nb] x 48 KB (dense and block-sparse)
-  size_t route_r;    // [2][N][heads] f32
   size_t route_pool; // [2][heads][nb][96] f32
+  size_t route_score;// [heads][nb][nb] u32 order keys (nb <= dit::route_topk_max_blocks(), else unused)
   size_t list;       // [heads][nqt][nb] i32
   size_t list_len;   // [heads][nqt] i32
   size_t total;
@@ -57,15 +57,16 @@ Layout make_layout(const Shape& s) {
   L.tab = 0;
   L.kvf = align256((size_t)(s.T + s.H + s.W) * dit::kRopeRow * sizeof(float));
   const size_t base = L.kvf + (size_t)s.heads * s.nb * dit::kTileImageBytes;
-  const size_t r_bytes = align256(2ull * s.N * s.heads * sizeof(float));
   const size_t pool_bytes = align256(2ull * s.heads * s.nb * dit::kHeadDim * sizeof(float));
-  L.route_r = base;
-  L.route_pool = base + r_bytes;
+  const size_t score_bytes =
+      s.nb <= dit::route_topk_max_blocks() ? align256((size_t)s.heads * s.nb * s.nb * sizeof(uint32_t)) : 0;
+  L.route_pool = base;
+  L.route_score = base + pool_bytes;
   const size_t list_bytes = align256((size_t)s.heads * s.nqt * s.nb * sizeof(int));
   const size_t len_bytes = align256((size_t)s.heads * s.nqt * sizeof(int));
   L.list = base;
   L.list_len = base + list_bytes;
-  L.total = base + std::max(r_bytes + pool_bytes, list_bytes + len_bytes);
+  L.total = base + std::max(pool_bytes + score_bytes, list_bytes + len_bytes);
   return L;
 }
 
@@ -295,8 +296,8 @@ dit_status dit_attn_route(const void* q, const void* k, const float* wq, const f
   a.eps = eps;
   a.nb = s.nb;
   a.keep = keep_count(s.nb, sparsity);
-  a.r = (float*)((char*)workspace + L.route_r);
   a.pooled = (float*)((char*)workspace + L.route_pool);
+  a.scores = (uint32_t*)((char*)workspace + L.route_score);
   a.mask = mask;
   const hipError_t e = dit::launch_route(a, stream);
   if (e != hipSuccess) return fail_hip(e, "router kernel launch");

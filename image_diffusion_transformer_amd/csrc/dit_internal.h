@@ -70,8 +70,8 @@ struct RouteArgs {
   float eps;
   int nb;
   int keep;
-  float* r;               // [2][N][heads] reciprocal RMS of q (0) and k (1)
   float* pooled;          // [2][heads][nb][96] block means of q (0) and k (1)
+  uint32_t* scores;       // [heads][nb][nb] order keys of the block scores (nb <= route_topk_max_blocks())
   unsigned char* mask;    // [heads][nb][nb]
 };
 
@@ -92,5 +92,9 @@ hipError_t launch_attn_dense(const AttnArgs& a, hipStream_t s);
 hipError_t launch_attn_sparse(const AttnArgs& a, hipStream_t s);
 hipError_t launch_compact(const CompactArgs& a, hipStream_t s);
 hipError_t launch_route(const RouteArgs& a, hipStream_t s);
+
+// Largest block count whose score rows the top-k kernel holds in registers; above it the router
+// scores and selects in one workgroup per row and needs no score matrix.
+constexpr int route_topk_max_blocks() { return 4096; }
 
 }  // namespace dit

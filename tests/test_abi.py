@@ -48,7 +48,9 @@ def test_keep_count_matches_golden(lib):
 def test_workspace_bytes(lib):
     n = dit.dit_attn_workspace_bytes(31, 48, 84, 56)
     N, nb = 124992, 977
-    assert n >= 2 * N * 56 * 4 + 2 * 56 * nb * 96 * 4      # router: rms + pooled vectors
+    assert n >= 56 * nb * 48 * 1024 + 2 * 56 * nb * 96 * 4 + 56 * nb * nb * 4   # images + router: pooled, scores
+    big = dit.dit_attn_workspace_bytes(1, 640, 820, 1)    # 4100 blocks: no score matrix
+    assert big < 4100 * 48 * 1024 + 2 * 4100 * 96 * 4 + 4100 * 4100 * 4
     assert n >= 56 * -(-N // 512) * nb * 4                  # sparse: KV lists per 512-token query tile
     assert n >= 56 * nb * 48 * 1024 + 56 * -(-N // 512) * nb * 4   # K^/V fragment images + sparse lists
     assert dit.dit_attn_workspace_bytes(31, 48, 84, 56, 128) == 0   # head_dim 128 unsupported
