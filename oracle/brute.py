@@ -72,3 +72,43 @@ def attention_joint(Q, K, V, wq, wk, q_pos, k_pos, theta=1e4, eps=1e-6):
             for c in range(d):
                 out[i][hd][c] = sum(ex[j] * float(V[j][hd][c]) for j in range(len(K))) / tot
     return out
+
+
+# ----------------------------------------------------------------------------
+# Operators around attention, one scalar at a time (checks oracle/block_ops.py).
+# ----------------------------------------------------------------------------
+
+def adaln_modulate(rows, shift, scale, eps=1e-6):
+    """LayerNorm without affine parameters, then * (1 + scale) + shift, per row of a nested list."""
+    out = []
+    for row in rows:
+        d = len(row)
+        mean = 0.0
+        for v in row:
+            mean += float(v)
+        mean /= d
+        var = 0.0
+        for v in row:
+            var += (float(v) - mean) ** 2
+        var /= d
+        inv = 1.0 / math.sqrt(var + eps)
+        out.append([(float(row[c]) - mean) * inv * (1.0 + float(scale[c])) + float(shift[c]) for c in range(d)])
+    return out
+
+
+def gated_residual(rows_x, rows_y, gate):
+    return [[float(x[c]) + float(gate[c]) * float(y[c]) for c in range(len(x))] for x, y in zip(rows_x, rows_y)]
+
+
+def swiglu(rows):
+    """First half of each row is the gate, second half the up projection."""
+    out = []
+    for row in rows:
+        f = len(row) // 2
+        res = []
+        for c in range(f):
+            g = float(row[c])
+            sig = 1.0 / (1.0 + math.exp(-g)) if g > -700.0 else 0.0
+            res.append(g * sig * float(row[f + c]))
+        out.append(res)
+    return out
