@@ -5,7 +5,7 @@ A step is one full layer: dense attention over the whole token grid for all head
 seeded synthetic bf16 tensors already resident in HBM when the timed region
 starts.  Prints ONE JSON line.
 
-    python bench.py [--steps K] [--warmup W] [--workload v5|image|v5s|v10s|v10d|...]
+    python bench.py [--steps K] [--warmup W] [--workload v5|image|v5s|v10s|v10d|v5h7|j_edit2|b_v5]
                     [--no-cpu-baseline] [--calib-copy]
 """
 from __future__ import annotations
@@ -36,14 +36,18 @@ DESCR = {
              "split by head over 8 GPUs"),
     "j_edit2": ("joint attention, image edit with 2 reference images: 65,536 target queries against "
                 "197,120 keys (512 text + 2 x 65,536 reference + 65,536 target tokens), 56 heads x 96"),
+    "b_v5": ("operators around attention at 124,992 tokens, hidden 5376, FFN 14336: AdaLN update, gated "
+             "residual + AdaLN update, SwiGLU, gated residual"),
 }
+BLOCK_METRIC = "GB/s of HBM (frac of 8 TB/s), AdaLN / gated residual / SwiGLU, 124,992 tokens, hidden 5376, FFN 14336"
 
 
 KERNEL_SRC = os.path.join(ROOT, "image_diffusion_transformer_amd", "csrc", "attn_fwd.hip")
+BLOCK_SRC = os.path.join(ROOT, "image_diffusion_transformer_amd", "csrc", "block_ops.hip")
 
 
-def kernel_source_sha256() -> str:
-    with open(KERNEL_SRC, "rb") as f:
+def kernel_source_sha256(path: str = KERNEL_SRC) -> str:
+    with open(path, "rb") as f:
         return hashlib.sha256(f.read()).hexdigest()
 
 
@@ -119,6 +123,97 @@ def bench_joint(args, torch, dit):
     print(json.dumps(result), flush=True)
 
 
+def bench_block(args, torch, dit):
+    """The fused operators around attention, each timed on its own; a step runs all four once."""
+    from synth import BLOCK_WORKLOADS, make_block_inputs
+    wl = BLOCK_WORKLOADS[args.workload]
+    t0 = time.time()
+    x = make_block_inputs(wl)
+    log(f"inputs {wl.name}: {wl.tokens} tokens, hidden {wl.hidden}, ffn {wl.ffn} in {time.time() - t0:.1f}s")
+    dev = torch.device("cuda:0")
+
+    def up(b):
+        return torch.from_numpy(b.bits.view(np.int16)).to(dev).view(torch.bfloat16)
+
+    X, Y, GU = up(x.x), up(x.y), up(x.gate_up)
+    gate, shift, scale = (torch.from_numpy(v).to(dev) for v in (x.gate, x.shift, x.scale))
+    h1, h2, xo, xo2 = (torch.empty_like(X) for _ in range(4))
+    out = torch.empty((wl.tokens, wl.ffn), dtype=torch.bfloat16, device=dev)
+    stream = torch.cuda.current_stream()
+    act = wl.tokens * wl.hidden * 2
+    ops = [  # name, call, algorithmic HBM bytes (activations; the fp32 vectors stay in cache)
+        ("adaln_modulate", lambda: dit.dit_adaln_modulate(X, shift, scale, wl.eps, h=h1), 2 * act),
+        ("gated_residual+adaln", lambda: dit.dit_gated_residual(X, Y, gate, shift, scale, wl.eps, x_out=xo, h=h2),
+         4 * act),
+        ("swiglu", lambda: dit.dit_swiglu(GU, out=out), 3 * wl.tokens * wl.ffn * 2),
+        ("gated_residual", lambda: dit.dit_gated_residual(xo, Y, gate, x_out=xo2, modulate=False), 3 * act),
+    ]
+    for _ in range(args.warmup):
+        for _, f, _ in ops:
+            f()
+    torch.cuda.synchronize()
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(len(ops) + 1)] for _ in range(args.steps)]
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        ev[i][0].record(stream)
+        for j, (_, f, _) in enumerate(ops):
+            f()
+            ev[i][j + 1].record(stream)
+    torch.cuda.synchronize()
+    ms_step = (time.perf_counter() - t0) * 1e3 / args.steps
+    per = {name: float(np.mean([e[j].elapsed_time(e[j + 1]) for e in ev])) for j, (name, _, _) in enumerate(ops)}
+    if args.calib_copy:
+        a = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
+        b = torch.empty_like(a)
+        b.copy_(a)
+        torch.cuda.synchronize()
+        del a, b
+    total = sum(b for _, _, b in ops)
+    gbs = total / (ms_step * 1e-3) / 1e9
+    dom = "swiglu"
+    dom_bytes = dict((n, b) for n, _, b in ops)[dom]
+    dom_gbs = dom_bytes / (per[dom] * 1e-3) / 1e9
+    traffic = None
+    tp = args.traffic or os.path.join(ROOT, "profiles", f"traffic_{wl.name}.json")
+    if os.path.exists(tp):
+        with open(tp) as f:
+            tr = json.load(f)
+        if tr.get("workload") == wl.name and tr.get("source_sha256") == kernel_source_sha256(BLOCK_SRC):
+            traffic = tr.get("bytes_per_launch")
+    result = {
+        "metric": BLOCK_METRIC, "value": round(gbs, 1), "unit": "GB/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": round(ms_step, 4), "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "bf16",
+        "data": "synthetic (seeded: residual stream N(0,1) with per-channel offsets and wide channels, branch N(0,1), "
+                "gate/up 2N(0,1), modulation vectors 0.5N(0,1))",
+        "config": {"workload": f"{wl.name}: {DESCR[wl.name]}", "tokens": wl.tokens, "hidden": wl.hidden,
+                   "ffn": wl.ffn},
+        "frac_of_hbm_peak": round(gbs / PEAK_HBM_GBS, 4),
+        "per_op_ms": {n: round(v, 4) for n, v in per.items()},
+        "per_op_gbs": {n: round(b / (per[n] * 1e-3) / 1e9, 1) for n, _, b in ops},
+        "roofline": {"bound": "hbm", "achieved": round(dom_gbs, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                     "frac": round(dom_gbs / PEAK_HBM_GBS, 4), "traffic": traffic, "kernel": "swiglu_kernel<7>",
+                     "kernel_ms": round(per[dom], 4), "bytes_per_launch": dom_bytes},
+    }
+    if not args.no_cpu_baseline:
+        from oracle import block_ops as O
+        rows = np.arange(0, wl.tokens, max(1, wl.tokens // 256))[:256]
+        cores = len(os.sched_getaffinity(0))
+        t0 = time.perf_counter()
+        xs, ys, gus = x.x[rows].astype(np.float64), x.y[rows].astype(np.float64), x.gate_up[rows].astype(np.float64)
+        O.adaln_modulate(xs, x.shift, x.scale, wl.eps)
+        r, _ = O.gated_residual_adaln(xs, ys, x.gate, x.shift, x.scale, wl.eps)
+        O.swiglu(gus)
+        O.gated_residual(r, ys, x.gate)
+        t_cpu = time.perf_counter() - t0
+        frac = len(rows) / wl.tokens
+        result["cpu_baseline"] = {
+            "value": round(total * frac / t_cpu / 1e9, 3), "unit": "GB/s", "cores": cores, "kind": "oracle",
+            "sample": f"fp64 numpy oracle of the four operators on {len(rows)} evenly spaced rows: {t_cpu:.2f} s "
+                      f"for {frac:.5f} of the step (same algorithmic bytes per row)"}
+    print(json.dumps(result), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -143,6 +238,8 @@ def main():
 
     if args.workload.startswith("j_"):
         return bench_joint(args, torch, dit)
+    if args.workload.startswith("b_"):
+        return bench_block(args, torch, dit)
 
     wl = WORKLOADS[args.workload]
     dev = torch.device("cuda:0")

@@ -22,7 +22,8 @@ STATUS_NAMES = {0: "DIT_OK", 1: "DIT_ERR_INVALID_ARG", 2: "DIT_ERR_UNSUPPORTED",
                 3: "DIT_ERR_WORKSPACE", 4: "DIT_ERR_HIP"}
 
 EXPORTS = ("dit_attn_workspace_bytes", "dit_attn_keep_count", "dit_attn_dense", "dit_attn_route",
-           "dit_attn_block_sparse", "dit_attn_joint_workspace_bytes", "dit_attn_joint", "dit_attn_last_error")
+           "dit_attn_block_sparse", "dit_attn_joint_workspace_bytes", "dit_attn_joint", "dit_attn_last_error",
+           "dit_adaln_modulate", "dit_gated_residual", "dit_swiglu")
 
 _lib = None
 _lock = threading.Lock()
@@ -58,6 +59,13 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
         lib.dit_attn_joint_workspace_bytes.restype = sz
         lib.dit_attn_joint.argtypes = [vp, vp, vp, vp, vp, vp, vp, i, i, i, i, i, f, f, vp, vp, sz, vp]
         lib.dit_attn_joint.restype = i
+        ll = ctypes.c_longlong
+        lib.dit_adaln_modulate.argtypes = [vp, vp, vp, ll, i, f, vp, vp]
+        lib.dit_adaln_modulate.restype = i
+        lib.dit_gated_residual.argtypes = [vp, vp, vp, vp, vp, ll, i, f, vp, vp, vp]
+        lib.dit_gated_residual.restype = i
+        lib.dit_swiglu.argtypes = [vp, ll, i, vp, vp]
+        lib.dit_swiglu.restype = i
         lib.dit_attn_last_error.argtypes = []
         lib.dit_attn_last_error.restype = ctypes.c_char_p
         _lib = lib
@@ -172,6 +180,47 @@ def dit_attn_joint(q, k, v, wq, wk, q_pos, k_pos, max_pos, rope_theta=10000.0, e
                                           nq, nk, heads, d, int(max_pos), rope_theta, eps, _ptr(o), _ptr(workspace),
                                           workspace.numel(), _stream(stream)))
     return o
+
+
+def _rows(x, name):
+    if x.dim() != 2 or x.dtype != torch.bfloat16 or not x.is_contiguous():
+        raise ValueError(f"{name} must be a contiguous bf16 [tokens, width] tensor")
+    return int(x.shape[0]), int(x.shape[1])
+
+
+def dit_adaln_modulate(x, shift, scale, eps=1e-6, h=None, stream=None):
+    """AdaLN update: h = LayerNorm(x) * (1 + scale) + shift; x bf16 [tokens, hidden], shift / scale fp32 [hidden]."""
+    tokens, hidden = _rows(x, "x")
+    if h is None:
+        h = torch.empty_like(x)
+    _check(load_library().dit_adaln_modulate(_ptr(x), _ptr(shift), _ptr(scale), tokens, hidden, eps, _ptr(h),
+                                             _stream(stream)))
+    return h
+
+
+def dit_gated_residual(x, y, gate, shift=None, scale=None, eps=1e-6, x_out=None, h=None, modulate=True, stream=None):
+    """x_out = x + gate * y and, if ``modulate``, h = LayerNorm(x_out) * (1 + scale) + shift from the float32 sum.
+    Returns (x_out, h); h is None without modulation.  x_out may be x (in-place)."""
+    tokens, hidden = _rows(x, "x")
+    if x_out is None:
+        x_out = torch.empty_like(x)
+    if modulate and h is None:
+        h = torch.empty_like(x)
+    if not modulate:
+        h = None
+    _check(load_library().dit_gated_residual(_ptr(x), _ptr(y), _ptr(gate), _ptr(shift), _ptr(scale), tokens, hidden,
+                                             eps, _ptr(x_out), _ptr(h), _stream(stream)))
+    return x_out, h
+
+
+def dit_swiglu(gate_up, out=None, stream=None):
+    """out = silu(g) * u for gate_up = [g | u], bf16 [tokens, 2 ffn] -> [tokens, ffn]."""
+    tokens, width = _rows(gate_up, "gate_up")
+    ffn = width // 2
+    if out is None:
+        out = torch.empty((tokens, ffn), dtype=gate_up.dtype, device=gate_up.device)
+    _check(load_library().dit_swiglu(_ptr(gate_up), tokens, ffn, _ptr(out), _stream(stream)))
+    return out
 
 
 def dit_attn_last_error() -> str:

@@ -28,6 +28,7 @@ SOURCES = [
     ("attn_fwd.hip", []),
     # Router arithmetic must be reproducible bit for bit: no contraction into FMAs.
     ("router.hip", ["-ffp-contract=off"]),
+    ("block_ops.hip", []),
     ("api.cpp", ["-x", "hip"]),
 ]
 

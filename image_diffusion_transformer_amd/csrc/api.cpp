@@ -1,7 +1,8 @@
-// Host side of the C ABI declared in include/dit_attn.h: argument validation,
-// workspace layout, host RoPE tables and kernel launches.  Nothing here computes
-// attention; every arithmetic step of the path runs in the gfx950 kernels.
+// Host side of the C ABI declared in include/dit_attn.h and include/dit_block.h: argument
+// validation, workspace layout, host RoPE tables and kernel launches.  Nothing here computes
+// attention or the block operators; every arithmetic step runs in the gfx950 kernels.
 #include "dit_attn.h"
+#include "dit_block.h"
 
 #include <cmath>
 #include <cstdarg>
@@ -395,6 +396,109 @@ dit_status dit_attn_joint(const void* q, const void* k, const void* v, const flo
   a.nb = j.nb;
   e = dit::launch_attn_dense(a, stream);
   if (e != hipSuccess) return fail_hip(e, "joint attention kernel launch");
+  return DIT_OK;
+}
+
+// ------------------------------------------------------------------------------------------------
+// Operators around attention (dit_block.h)
+
+namespace {
+
+constexpr int kMaxHidden = 8192;
+
+// [p, p + bytes) and [q, q + bytes2) share a byte.
+bool overlaps(const void* p, size_t bytes, const void* q, size_t bytes2) {
+  const uintptr_t a = (uintptr_t)p, b = (uintptr_t)q;
+  return a < b + bytes2 && b < a + bytes;
+}
+
+dit_status check_rows(long long tokens, int width, const char* what) {
+  if (tokens < 0) return fail(DIT_ERR_INVALID_ARG, "tokens must be >= 0 (got %lld)", tokens);
+  if (width < 8 || width % 8 != 0) return fail(DIT_ERR_INVALID_ARG, "%s must be a positive multiple of 8 (got %d)", what, width);
+  if (tokens > (1ll << 40) / width) return fail(DIT_ERR_UNSUPPORTED, "tokens * %s too large", what);
+  return DIT_OK;
+}
+
+}  // namespace
+
+dit_status dit_adaln_modulate(const void* x, const float* shift, const float* scale, long long tokens, int hidden,
+                              float eps, void* h, void* hip_stream) {
+  g_err.clear();
+  dit_status st = check_rows(tokens, hidden, "hidden");
+  if (st != DIT_OK) return st;
+  if (hidden > kMaxHidden) return fail(DIT_ERR_UNSUPPORTED, "hidden %d exceeds %d", hidden, kMaxHidden);
+  if (!x || !shift || !scale || !h) return fail(DIT_ERR_INVALID_ARG, "null x, shift, scale or h");
+  if (!aligned16(x) || !aligned16(shift) || !aligned16(scale) || !aligned16(h))
+    return fail(DIT_ERR_INVALID_ARG, "x, shift, scale and h must be 16-byte aligned");
+  if (!std::isfinite(eps) || eps < 0.f) return fail(DIT_ERR_INVALID_ARG, "eps must be finite and >= 0");
+  const size_t bytes = (size_t)tokens * hidden * 2;
+  if (overlaps(x, bytes, h, bytes)) return fail(DIT_ERR_INVALID_ARG, "h overlaps x");
+  if (tokens == 0) return DIT_OK;
+  dit::BlockArgs a{};
+  a.x = (const uint16_t*)x;
+  a.shift = shift;
+  a.scale = scale;
+  a.h = (uint16_t*)h;
+  a.tokens = tokens;
+  a.hidden = hidden;
+  a.eps = eps;
+  const hipError_t e = dit::launch_adaln(a, false, true, (hipStream_t)hip_stream);
+  if (e != hipSuccess) return fail_hip(e, "AdaLN kernel launch");
+  return DIT_OK;
+}
+
+dit_status dit_gated_residual(const void* x, const void* y, const float* gate, const float* shift, const float* scale,
+                              long long tokens, int hidden, float eps, void* x_out, void* h, void* hip_stream) {
+  g_err.clear();
+  dit_status st = check_rows(tokens, hidden, "hidden");
+  if (st != DIT_OK) return st;
+  if (hidden > kMaxHidden) return fail(DIT_ERR_UNSUPPORTED, "hidden %d exceeds %d", hidden, kMaxHidden);
+  if (!x || !y || !gate || !x_out) return fail(DIT_ERR_INVALID_ARG, "null x, y, gate or x_out");
+  if (h && (!shift || !scale)) return fail(DIT_ERR_INVALID_ARG, "h needs shift and scale");
+  if (!aligned16(x) || !aligned16(y) || !aligned16(gate) || !aligned16(x_out) || (h && !aligned16(h)) ||
+      (h && (!aligned16(shift) || !aligned16(scale))))
+    return fail(DIT_ERR_INVALID_ARG, "tensors and vectors must be 16-byte aligned");
+  if (h && (!std::isfinite(eps) || eps < 0.f)) return fail(DIT_ERR_INVALID_ARG, "eps must be finite and >= 0");
+  const size_t bytes = (size_t)tokens * hidden * 2;
+  if (x_out != x && overlaps(x_out, bytes, x, bytes))
+    return fail(DIT_ERR_INVALID_ARG, "x_out must be x itself or not overlap it");
+  if (overlaps(x_out, bytes, y, bytes)) return fail(DIT_ERR_INVALID_ARG, "x_out overlaps y");
+  if (h && (overlaps(h, bytes, x, bytes) || overlaps(h, bytes, y, bytes) || overlaps(h, bytes, x_out, bytes)))
+    return fail(DIT_ERR_INVALID_ARG, "h overlaps x, y or x_out");
+  if (tokens == 0) return DIT_OK;
+  dit::BlockArgs a{};
+  a.x = (const uint16_t*)x;
+  a.y = (const uint16_t*)y;
+  a.gate = gate;
+  a.shift = shift;
+  a.scale = scale;
+  a.x_out = (uint16_t*)x_out;
+  a.h = (uint16_t*)h;
+  a.tokens = tokens;
+  a.hidden = hidden;
+  a.eps = eps;
+  const hipError_t e = dit::launch_adaln(a, true, h != nullptr, (hipStream_t)hip_stream);
+  if (e != hipSuccess) return fail_hip(e, "gated residual kernel launch");
+  return DIT_OK;
+}
+
+dit_status dit_swiglu(const void* gate_up, long long tokens, int ffn, void* out, void* hip_stream) {
+  g_err.clear();
+  dit_status st = check_rows(tokens, ffn, "ffn");
+  if (st != DIT_OK) return st;
+  if (ffn > (1 << 28)) return fail(DIT_ERR_UNSUPPORTED, "ffn %d too large", ffn);
+  if (!gate_up || !out) return fail(DIT_ERR_INVALID_ARG, "null gate_up or out");
+  if (!aligned16(gate_up) || !aligned16(out)) return fail(DIT_ERR_INVALID_ARG, "gate_up and out must be 16-byte aligned");
+  if (overlaps(gate_up, (size_t)tokens * ffn * 4, out, (size_t)tokens * ffn * 2))
+    return fail(DIT_ERR_INVALID_ARG, "out overlaps gate_up");
+  if (tokens == 0) return DIT_OK;
+  dit::SwigluArgs a{};
+  a.gu = (const uint16_t*)gate_up;
+  a.out = (uint16_t*)out;
+  a.tokens = tokens;
+  a.ffn = ffn;
+  const hipError_t e = dit::launch_swiglu(a, (hipStream_t)hip_stream);
+  if (e != hipSuccess) return fail_hip(e, "SwiGLU kernel launch");
   return DIT_OK;
 }
 

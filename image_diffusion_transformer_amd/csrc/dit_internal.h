@@ -82,6 +82,28 @@ struct CompactArgs {
   int heads, nb, nqt, group;   // group = router blocks per query tile
 };
 
+// Operators around attention: AdaLN update and gated residual (one wave per token row).
+struct BlockArgs {
+  const uint16_t* x;      // bf16 [tokens][hidden]
+  const uint16_t* y;      // bf16 [tokens][hidden] branch output (gated residual)
+  const float* gate;      // [hidden]
+  const float* shift;     // [hidden]
+  const float* scale;     // [hidden]
+  uint16_t* x_out;        // bf16 [tokens][hidden] residual sum (may equal x)
+  uint16_t* h;            // bf16 [tokens][hidden] AdaLN update
+  long long tokens;
+  int hidden;             // multiple of 8, <= 8192
+  float eps;
+};
+
+struct SwigluArgs {
+  const uint16_t* gu;     // bf16 [tokens][2 ffn]: gate then up projection
+  uint16_t* out;          // bf16 [tokens][ffn]
+  long long tokens;
+  int ffn;                // multiple of 8
+  int chunks;             // workgroups per token row (set by launch_swiglu)
+};
+
 // Bytes of one (head, 128-key tile) fragment image: 48 fragments of 64 lanes x 16 bytes.
 constexpr size_t kTileImageBytes = 48 * 1024;
 
@@ -92,6 +114,8 @@ hipError_t launch_attn_dense(const AttnArgs& a, hipStream_t s);
 hipError_t launch_attn_sparse(const AttnArgs& a, hipStream_t s);
 hipError_t launch_compact(const CompactArgs& a, hipStream_t s);
 hipError_t launch_route(const RouteArgs& a, hipStream_t s);
+hipError_t launch_adaln(const BlockArgs& a, bool resid, bool norm, hipStream_t s);
+hipError_t launch_swiglu(SwigluArgs a, hipStream_t s);
 
 // Largest block count whose score rows the top-k kernel holds in registers; above it the router
 // scores and selects in one workgroup per row and needs no score matrix.

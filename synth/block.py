@@ -49,6 +49,9 @@ BLOCK_WORKLOADS = {
         BlockWorkload("b_mid", 1000, 5376, 14336, seed=42, notes="1000 tokens, several waves per CU"),
         BlockWorkload("b_odd", 19, 1032, 776, seed=43,
                       notes="hidden 1032 and FFN 776: widths that are multiples of 8 but not of 64"),
+        BlockWorkload("b_wide", 29, 8184, 16400, seed=45,
+                      notes="hidden 8184 (16 vectors per lane, last one ragged) and FFN 16400 (two "
+                            "workgroups per row)"),
         BlockWorkload("b_v5", 124992, 5376, 14336, seed=44,
                       notes="124,992 tokens (5 s 1344x768 clip) at hidden 5376, FFN 14336"),
     ]

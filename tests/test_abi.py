@@ -10,7 +10,8 @@ import pytest
 import image_diffusion_transformer_amd as dit
 from image_diffusion_transformer_amd import _binding as B
 
-HEADER = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))), "include", "dit_attn.h")
+INCLUDE = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))), "include")
+HEADERS = [os.path.join(INCLUDE, "dit_attn.h"), os.path.join(INCLUDE, "dit_block.h")]
 
 
 @pytest.fixture(scope="module")
@@ -22,9 +23,11 @@ def lib():
 
 
 def header_functions():
-    text = open(HEADER).read()
-    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
-    return sorted(set(re.findall(r"\b(dit_attn_\w+)\s*\(", text)))
+    names = set()
+    for h in HEADERS:
+        text = re.sub(r"/\*.*?\*/", "", open(h).read(), flags=re.S)
+        names |= set(re.findall(r"\b(dit_\w+)\s*\(", text))
+    return sorted(names)
 
 
 def test_every_declared_symbol_is_exported(lib):
@@ -184,3 +187,57 @@ def test_joint_workspace_bytes(lib):
     assert n >= 56 * 1540 * 48 * 1024 + 515 * 32 * 4          # fragment images of 1540 key tiles + table
     assert dit.dit_attn_joint_workspace_bytes(10, 10, 2, 96, 0) == 0
     assert dit.dit_attn_joint_workspace_bytes(10, 0, 2, 96, 4) == 0
+
+
+# ---------------------------------------------------------------------------------- operators around attention
+def _adaln(lib, **kw):
+    a = dict(x=FAKE, shift=FAKE, scale=FAKE, tokens=10, hidden=5376, eps=1e-6, h=FAKE + (1 << 24), stream=None)
+    a.update(kw)
+    return lib.dit_adaln_modulate(a["x"], a["shift"], a["scale"], a["tokens"], a["hidden"], a["eps"], a["h"],
+                                  a["stream"])
+
+
+def _resid(lib, **kw):
+    a = dict(x=FAKE, y=FAKE + (1 << 24), gate=FAKE, shift=FAKE, scale=FAKE, tokens=10, hidden=5376, eps=1e-6,
+             x_out=FAKE, h=FAKE + (2 << 24), stream=None)
+    a.update(kw)
+    return lib.dit_gated_residual(a["x"], a["y"], a["gate"], a["shift"], a["scale"], a["tokens"], a["hidden"],
+                                  a["eps"], a["x_out"], a["h"], a["stream"])
+
+
+def _swiglu(lib, **kw):
+    a = dict(gu=FAKE, tokens=10, ffn=14336, out=FAKE + (1 << 24), stream=None)
+    a.update(kw)
+    return lib.dit_swiglu(a["gu"], a["tokens"], a["ffn"], a["out"], a["stream"])
+
+
+@pytest.mark.parametrize("call,kw,status,text", [
+    (_adaln, dict(x=None), B.DIT_ERR_INVALID_ARG, "null"),
+    (_adaln, dict(hidden=5370), B.DIT_ERR_INVALID_ARG, "multiple of 8"),
+    (_adaln, dict(hidden=0), B.DIT_ERR_INVALID_ARG, "multiple of 8"),
+    (_adaln, dict(hidden=8200), B.DIT_ERR_UNSUPPORTED, "exceeds"),
+    (_adaln, dict(tokens=-1), B.DIT_ERR_INVALID_ARG, "tokens"),
+    (_adaln, dict(eps=float("nan")), B.DIT_ERR_INVALID_ARG, "eps"),
+    (_adaln, dict(scale=FAKE + 4), B.DIT_ERR_INVALID_ARG, "aligned"),
+    (_adaln, dict(h=FAKE + 1024), B.DIT_ERR_INVALID_ARG, "overlaps"),
+    (_resid, dict(gate=None), B.DIT_ERR_INVALID_ARG, "null"),
+    (_resid, dict(shift=None), B.DIT_ERR_INVALID_ARG, "shift and scale"),
+    (_resid, dict(x_out=FAKE + 1024), B.DIT_ERR_INVALID_ARG, "x itself"),
+    (_resid, dict(x_out=FAKE + (1 << 24)), B.DIT_ERR_INVALID_ARG, "overlaps y"),
+    (_resid, dict(h=FAKE + 64), B.DIT_ERR_INVALID_ARG, "h overlaps"),
+    (_resid, dict(y=FAKE + (1 << 24) + 8), B.DIT_ERR_INVALID_ARG, "aligned"),
+    (_swiglu, dict(ffn=12), B.DIT_ERR_INVALID_ARG, "multiple of 8"),
+    (_swiglu, dict(out=FAKE + 4096), B.DIT_ERR_INVALID_ARG, "overlaps"),
+    (_swiglu, dict(gu=None), B.DIT_ERR_INVALID_ARG, "null"),
+])
+def test_block_validation_errors(lib, call, kw, status, text):
+    assert call(lib, **kw) == status
+    assert text in B.dit_attn_last_error()
+
+
+def test_block_zero_tokens_queue_nothing(lib):
+    # valid arguments with no rows: success without touching a device
+    assert _adaln(lib, tokens=0) == B.DIT_OK
+    assert _resid(lib, tokens=0) == B.DIT_OK
+    assert _resid(lib, tokens=0, h=None, shift=None, scale=None) == B.DIT_OK
+    assert _swiglu(lib, tokens=0) == B.DIT_OK
