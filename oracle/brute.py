@@ -9,19 +9,25 @@ from __future__ import annotations
 import math
 
 
+# channel widths of the t, h, w rotation chunks: equal thirds at 96, (44, 42, 42) at 128
+_WIDTHS = {96: (32, 32, 32), 128: (44, 42, 42)}
+
+
 def _normalise_rotate(vec, weight, t, h, w, theta, eps):
     d = len(vec)
     ms = sum(x * x for x in vec) / d
     inv = 1.0 / math.sqrt(ms + eps)
     xn = [vec[c] * weight[c] * inv for c in range(d)]
     out = list(xn)
-    for axis, pos in enumerate((t, h, w)):
-        for i in range(16):
-            e = 32 * axis + 2 * i
-            ang = pos * theta ** (-(2.0 * i) / 32.0)
+    start = 0
+    for pos, width in zip((t, h, w), _WIDTHS[d]):
+        for i in range(width // 2):
+            e = start + 2 * i
+            ang = pos * theta ** (-(2.0 * i) / width)
             co, si = math.cos(ang), math.sin(ang)
             out[e] = xn[e] * co - xn[e + 1] * si
             out[e + 1] = xn[e] * si + xn[e + 1] * co
+        start += width
     return out
 
 

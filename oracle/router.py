@@ -25,15 +25,16 @@ S. Figueroa, "When is double rounding innocuous?", 1995).
 ``route_mask_f32`` is a second, independent evaluation in numpy float32
 arithmetic; the two must agree bitwise.
 
-  R0 c[a][p][i] = fl(cos(p * theta^(-2i/32))), s likewise; angle in fp64,
-     cos/sin from the C library (Python's math module).
-  R1 ss = 0; for c in 0..95: ss = fl(ss + fl(x_c * x_c))
-     ms = fl(ss / 96); r = fl(1 / fl(sqrt(fl(ms + eps))))
+  R0 c[a][p][i] = fl(cos(p * theta^(-2i/w_a))), s likewise, w_a the channel width of axis a
+     (32 each at head dim d = 96; 44, 42, 42 at d = 128, see attention.ROPE_SPLITS); angle in
+     fp64, cos/sin from the C library (Python's math module).
+  R1 ss = 0; for c in 0..d-1: ss = fl(ss + fl(x_c * x_c))
+     ms = fl(ss / d); r = fl(1 / fl(sqrt(fl(ms + eps))))
   R2 xh_c = fl(fl(x_c * r) * w_c)
      y_e = fl(fl(xh_e * c) - fl(xh_f * s)); y_f = fl(fl(xh_e * s) + fl(xh_f * c))
   R3 acc = 0; for tokens n of block b ascending: acc = fl(acc + y_c[n])
      mean = fl(acc / count_b)
-  R4 acc = 0; for c in 0..95: acc = fl(acc + fl(qbar_i,c * kbar_j,c)); s_ii = +inf
+  R4 acc = 0; for c in 0..d-1: acc = fl(acc + fl(qbar_i,c * kbar_j,c)); s_ii = +inf
   R5 top-`keep` selection under (score desc, j asc); -0.0 == +0.0.
 """
 from __future__ import annotations
@@ -42,9 +43,7 @@ import math
 
 import numpy as np
 
-D = 96
-AXIS = 32
-PAIRS = 16
+from .attention import rope_split
 
 
 def keep_count(nb: int, sparsity: float) -> int:
@@ -57,15 +56,16 @@ def keep_count(nb: int, sparsity: float) -> int:
     return max(1, min(nb, k))
 
 
-def rope_tables_f32(T: int, H: int, W: int, theta: float):
-    """R0: fp32 cos/sin tables per axis, [T|H|W][16] each, returned as float64 arrays."""
+def rope_tables_f32(T: int, H: int, W: int, theta: float, split=(32, 32, 32)):
+    """R0: fp32 cos/sin tables per axis, [T|H|W][width/2] each, returned as float64 arrays."""
     th = float(np.float32(theta))
     out = []
-    for npos in (T, H, W):
-        c = np.empty((npos, PAIRS), dtype=np.float64)
-        s = np.empty((npos, PAIRS), dtype=np.float64)
-        for i in range(PAIRS):
-            inv = th ** (-2 * i / AXIS)
+    for npos, width in zip((T, H, W), split):
+        pairs = width // 2
+        c = np.empty((npos, pairs), dtype=np.float64)
+        s = np.empty((npos, pairs), dtype=np.float64)
+        for i in range(pairs):
+            inv = th ** (-2 * i / width)
             for p in range(npos):
                 ang = p * inv
                 c[p, i] = float(np.float32(math.cos(ang)))
@@ -85,31 +85,33 @@ def _positions(T, H, W):
 
 
 def _prepare_f64r(x, w, tabs, T, H, W, eps):
-    """R1 + R2 for one head: x [N, 96] -> y [N, 96] (fp32 values in float64)."""
+    """R1 + R2 for one head: x [N, d] -> y [N, d] (fp32 values in float64)."""
     x = np.asarray(x, dtype=np.float64)
-    N = x.shape[0]
+    N, D = x.shape
     ss = np.zeros(N)
     for c in range(D):
         ss = _fl(ss + _fl(x[:, c] * x[:, c]))
-    ms = _fl(ss / 96.0)
+    ms = _fl(ss / float(D))
     r = _fl(1.0 / _fl(np.sqrt(_fl(ms + float(np.float32(eps))))))
     w = np.asarray(w, dtype=np.float32).astype(np.float64)
     xh = _fl(_fl(x * r[:, None]) * w[None, :])
     y = np.empty_like(xh)
     pos = _positions(T, H, W)
-    for a in range(3):
-        c = tabs[a][0][pos[a]]   # [N, 16]
+    o = 0
+    for a, width in enumerate(rope_split(D)):
+        c = tabs[a][0][pos[a]]   # [N, width/2]
         s = tabs[a][1][pos[a]]
-        e = xh[:, a * AXIS:(a + 1) * AXIS:2]
-        f = xh[:, a * AXIS + 1:(a + 1) * AXIS:2]
-        y[:, a * AXIS:(a + 1) * AXIS:2] = _fl(_fl(e * c) - _fl(f * s))
-        y[:, a * AXIS + 1:(a + 1) * AXIS:2] = _fl(_fl(e * s) + _fl(f * c))
+        e = xh[:, o:o + width:2]
+        f = xh[:, o + 1:o + width:2]
+        y[:, o:o + width:2] = _fl(_fl(e * c) - _fl(f * s))
+        y[:, o + 1:o + width:2] = _fl(_fl(e * s) + _fl(f * c))
+        o += width
     return y
 
 
 def _pool_f64r(y, block):
     """R3: sequential fp32 block sums, then division by the true token count."""
-    N = y.shape[0]
+    N, D = y.shape
     nb = -(-N // block)
     pad = nb * block - N
     yp = np.concatenate([y, np.zeros((pad, D))]) if pad else y
@@ -125,7 +127,7 @@ def _pool_f64r(y, block):
 
 def _scores_f64r(qbar, kbar):
     """R4: sequential fp32 dot products, diagonal forced to +inf."""
-    nb = qbar.shape[0]
+    nb, D = qbar.shape
     acc = np.zeros((nb, nb))
     for c in range(D):
         acc = _fl(acc + _fl(qbar[:, c][:, None] * kbar[:, c][None, :]))
@@ -147,7 +149,7 @@ def select_topk(scores: np.ndarray, keep: int) -> np.ndarray:
 
 def route_scores(Q, K, wq, wk, T, H, W, theta=1e4, eps=1e-6, block=128, heads=None):
     """R0-R4 per head: list of fp32-exact score matrices [nb, nb] (float64 holding fp32 values)."""
-    tabs = rope_tables_f32(T, H, W, theta)
+    tabs = rope_tables_f32(T, H, W, theta, rope_split(Q.shape[2]))
     nheads = Q.shape[1]
     heads = range(nheads) if heads is None else heads
     out = []
@@ -176,13 +178,16 @@ def route_scores_f32(Q, K, wq, wk, T, H, W, theta=1e4, eps=1e-6, block=128, head
     f = np.float32
     N = T * H * W
     nb = -(-N // block)
+    D = Q.shape[2]
+    split = rope_split(D)
     th = float(np.float32(theta))
     tabs = []
-    for npos in (T, H, W):
-        c = np.array([[math.cos(p * th ** (-2 * i / AXIS)) for i in range(PAIRS)] for p in range(npos)],
-                     dtype=np.float32).reshape(npos, PAIRS)
-        s = np.array([[math.sin(p * th ** (-2 * i / AXIS)) for i in range(PAIRS)] for p in range(npos)],
-                     dtype=np.float32).reshape(npos, PAIRS)
+    for npos, width in zip((T, H, W), split):
+        pairs = width // 2
+        c = np.array([[math.cos(p * th ** (-2 * i / width)) for i in range(pairs)] for p in range(npos)],
+                     dtype=np.float32).reshape(npos, pairs)
+        s = np.array([[math.sin(p * th ** (-2 * i / width)) for i in range(pairs)] for p in range(npos)],
+                     dtype=np.float32).reshape(npos, pairs)
         tabs.append((c, s))
     pos = _positions(T, H, W)
     eps32 = f(eps)
@@ -195,17 +200,19 @@ def route_scores_f32(Q, K, wq, wk, T, H, W, theta=1e4, eps=1e-6, block=128, head
         ss = np.zeros(N, dtype=np.float32)
         for c in range(D):
             ss = ss + x[:, c] * x[:, c]
-        ms = ss / f(96.0)
+        ms = ss / f(D)
         r = f(1.0) / np.sqrt(ms + eps32)
         xh = (x * r[:, None]) * np.asarray(w, dtype=np.float32)[None, :]
         y = np.empty_like(xh)
-        for a in range(3):
+        off = 0
+        for a, width in enumerate(split):
             c = tabs[a][0][pos[a]]
             s = tabs[a][1][pos[a]]
-            e = xh[:, a * AXIS:(a + 1) * AXIS:2]
-            o = xh[:, a * AXIS + 1:(a + 1) * AXIS:2]
-            y[:, a * AXIS:(a + 1) * AXIS:2] = e * c - o * s
-            y[:, a * AXIS + 1:(a + 1) * AXIS:2] = e * s + o * c
+            e = xh[:, off:off + width:2]
+            o = xh[:, off + 1:off + width:2]
+            y[:, off:off + width:2] = e * c - o * s
+            y[:, off + 1:off + width:2] = e * s + o * c
+            off += width
         return y
 
     def pool(y):

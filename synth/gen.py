@@ -47,6 +47,7 @@ class Workload:
     theta: float = 10000.0
     eps: float = 1e-6
     fp32_inputs: bool = False    # the tiny grid also keeps its float32 draw
+    head_dim: int = HEAD_DIM     # 96 (the model's); 128 for the head-dim-128 instantiation
     notes: str = field(default="", compare=False)
 
     @property
@@ -80,6 +81,15 @@ WORKLOADS = {
         Workload("s2", 3, 16, 16, 3, seed=11, smooth=True, notes="N=768 (6 full blocks)"),
         Workload("s3", 4, 12, 20, 4, seed=12, smooth=True, notes="N=960 (tail 64)"),
         Workload("s4", 5, 24, 40, 2, seed=13, smooth=True, notes="N=4800 (tail 64), 38 blocks"),
+        # head dim 128 (42 heads x 128 = the same 5376 hidden width)
+        Workload("t128", 2, 4, 4, 2, seed=30, smooth=False, head_dim=128, notes="2x4x4 grid, head dim 128"),
+        Workload("s1_128", 2, 10, 10, 2, seed=31, smooth=True, head_dim=128, notes="N=200 (tail 72), head dim 128"),
+        Workload("s3_128", 4, 12, 20, 3, seed=32, smooth=True, head_dim=128, notes="N=960 (tail 64), head dim 128"),
+        Workload("s4_128", 5, 24, 40, 2, seed=33, smooth=True, head_dim=128, notes="N=4800, 38 blocks, head dim 128"),
+        Workload("v5d128", 31, 48, 84, 42, seed=34, smooth=True, head_dim=128,
+                 notes="5 s video grid, 42 heads x 128 (hidden 5376), dense"),
+        Workload("v5s128", 31, 48, 84, 42, seed=34, smooth=True, head_dim=128, mode="sparse", sparsity=0.75,
+                 notes="same tensors as v5d128, block-sparse at sparsity 0.75"),
     ]
 }
 
@@ -127,7 +137,7 @@ class Inputs:
     v32: np.ndarray | None = None
 
 
-def _smooth_params(seed: int, heads: int):
+def _smooth_params(seed: int, heads: int, d: int = HEAD_DIM):
     """Frequencies, phases and per-(tensor, head, channel) signs of the three sinusoids."""
     g = np.random.Generator(np.random.PCG64(np.random.SeedSequence([seed, 99])))
     freqs, phases = [], []
@@ -138,14 +148,14 @@ def _smooth_params(seed: int, heads: int):
                 break
         freqs.append(f)
         phases.append(g.uniform(0.0, 2.0 * math.pi))
-    signs = g.choice(np.array([-1.0, 1.0]), size=(3, heads, HEAD_DIM, 3))  # [tensor, head, c, m]
+    signs = g.choice(np.array([-1.0, 1.0]), size=(3, heads, d, 3))  # [tensor, head, c, m]
     return np.array(freqs, dtype=np.float64), np.array(phases), signs
 
 
-def _weights(seed: int):
+def _weights(seed: int, d: int = HEAD_DIM):
     g = np.random.Generator(np.random.PCG64(np.random.SeedSequence([seed, 7])))
-    wq = (1.0 + 0.1 * g.standard_normal(HEAD_DIM)).astype(np.float32)
-    wk = (1.0 + 0.1 * g.standard_normal(HEAD_DIM)).astype(np.float32)
+    wq = (1.0 + 0.1 * g.standard_normal(d)).astype(np.float32)
+    wk = (1.0 + 0.1 * g.standard_normal(d)).astype(np.float32)
     return wq, wk
 
 
@@ -153,7 +163,8 @@ def _fill_chunk(wl: Workload, tensor: int, chunk: int, smooth, out_bits, out_f32
     n0 = chunk * CHUNK_TOKENS
     n1 = min(wl.N, n0 + CHUNK_TOKENS)
     g = np.random.Generator(np.random.PCG64(np.random.SeedSequence([wl.seed, tensor, chunk])))
-    x = g.standard_normal((n1 - n0, wl.heads, HEAD_DIM), dtype=np.float32)
+    d = wl.head_dim
+    x = g.standard_normal((n1 - n0, wl.heads, d), dtype=np.float32)
     if smooth is not None:
         freqs, phases, signs = smooth
         n = np.arange(n0, n1)
@@ -163,9 +174,9 @@ def _fill_chunk(wl: Workload, tensor: int, chunk: int, smooth, out_bits, out_f32
         arg = (freqs[:, 0:1] * (t / wl.T) + freqs[:, 1:2] * (h / wl.H)
                + freqs[:, 2:3] * (w / wl.W))                      # [3, n]
         F = np.sin(2.0 * math.pi * arg + phases[:, None])           # [3, n]
-        s = signs[tensor].reshape(wl.heads * HEAD_DIM, 3)           # [heads*96, 3]
-        add = 0.5 * (F.T @ s.T)                                     # [n, heads*96]
-        x += add.reshape(n1 - n0, wl.heads, HEAD_DIM).astype(np.float32)
+        s = signs[tensor].reshape(wl.heads * d, 3)                  # [heads*d, 3]
+        add = 0.5 * (F.T @ s.T)                                     # [n, heads*d]
+        x += add.reshape(n1 - n0, wl.heads, d).astype(np.float32)
     out_bits[n0:n1] = f32_to_bf16_bits(x)
     if out_f32 is not None:
         out_f32[n0:n1] = x
@@ -175,10 +186,11 @@ def make_inputs(wl: Workload | str, threads: int | None = None) -> Inputs:
     """Draw the seeded inputs of a workload (host memory)."""
     if isinstance(wl, str):
         wl = WORKLOADS[wl]
-    smooth = _smooth_params(wl.seed, wl.heads) if wl.smooth else None
+    d = wl.head_dim
+    smooth = _smooth_params(wl.seed, wl.heads, d) if wl.smooth else None
     nchunks = -(-wl.N // CHUNK_TOKENS)
-    bits = [np.empty((wl.N, wl.heads, HEAD_DIM), dtype=np.uint16) for _ in range(3)]
-    f32 = ([np.empty((wl.N, wl.heads, HEAD_DIM), dtype=np.float32) for _ in range(3)]
+    bits = [np.empty((wl.N, wl.heads, d), dtype=np.uint16) for _ in range(3)]
+    f32 = ([np.empty((wl.N, wl.heads, d), dtype=np.float32) for _ in range(3)]
            if wl.fp32_inputs else [None] * 3)
     jobs = [(t, c) for t in range(3) for c in range(nchunks)]
     if threads is None:
@@ -189,7 +201,7 @@ def make_inputs(wl: Workload | str, threads: int | None = None) -> Inputs:
     else:
         with ThreadPoolExecutor(threads) as ex:
             list(ex.map(lambda tc: _fill_chunk(wl, tc[0], tc[1], smooth, bits[tc[0]], f32[tc[0]]), jobs))
-    wq, wk = _weights(wl.seed)
+    wq, wk = _weights(wl.seed, d)
     return Inputs(wl, BF16Tensor(bits[0]), BF16Tensor(bits[1]), BF16Tensor(bits[2]), wq, wk,
                   *f32)
 

@@ -240,13 +240,14 @@ def test_keep_count_golden():
 
 def test_model_shape_golden():
     g = json.load(open(os.path.join(GOLD, "model_shape.json")))
-    assert g["hidden"] // g["heads"] == g["head_dim"] == A.D == R.D
+    assert g["hidden"] // g["heads"] == g["head_dim"] == A.D
+    assert A.rope_split(A.D) == (g["rope_axis_dim"],) * g["rope_axes"]
     assert g["rope_axes"] * g["rope_axis_dim"] == A.D and A.AXIS == g["rope_axis_dim"]
 
 
-@pytest.mark.parametrize("name", ["s1", "s3"])
+@pytest.mark.parametrize("name", ["s1", "s3", "s1_128"])
 def test_router_score_is_mean_block_logit(name):
-    """Bilinearity: qbar_i . kbar_j / sqrt(96) equals the mean logit of block pair (i, j), ragged tail included."""
+    """Bilinearity: qbar_i . kbar_j / sqrt(d) equals the mean logit of block pair (i, j), ragged tail included."""
     x = make_inputs(name)
     wl = x.workload
     N, nb = wl.N, wl.nb
@@ -256,7 +257,7 @@ def test_router_score_is_mean_block_logit(name):
         for i in range(nb):
             for j in range(nb):
                 blk = L[i * 128:min(N, (i + 1) * 128), j * 128:min(N, (j + 1) * 128)]
-                assert s[i, j] / math.sqrt(96) == pytest.approx(blk.mean(), rel=1e-11, abs=1e-13)
+                assert s[i, j] / math.sqrt(wl.head_dim) == pytest.approx(blk.mean(), rel=1e-11, abs=1e-13)
 
 
 def test_router_fp32_spec_close_to_exact():
@@ -271,7 +272,7 @@ def test_router_fp32_spec_close_to_exact():
         assert np.max(np.abs(f - ex)) <= 1e-5 * np.max(np.abs(ex))
 
 
-@pytest.mark.parametrize("name", ["s1", "s2", "s3", "s4"])
+@pytest.mark.parametrize("name", ["s1", "s2", "s3", "s4", "s3_128"])
 def test_router_two_fp32_evaluations_bitwise(name):
     x = make_inputs(name)
     wl = x.workload
@@ -388,3 +389,85 @@ def test_joint_single_key_gives_v():
     wl = x.workload
     got = A.attention_joint(x.q, x.k[3:4], x.v[3:4], x.wq, x.wk, x.q_pos, x.k_pos[3:4], wl.theta, wl.eps)
     assert np.array_equal(got, np.broadcast_to(np.asarray(x.v[3:4], np.float64), got.shape))
+
+
+# ----------------------------------------------------------------------------- head dim 128
+SPLIT128 = ((0, 44), (44, 42), (86, 42))          # (first channel, width) of the t, h, w chunks
+
+
+@pytest.mark.parametrize("axis", [0, 1, 2])
+def test_rope128_worked_rotation(axis):
+    """d = 128: pair 0 of an axis chunk turns by pos rad; pair i of a chunk of width c turns by
+    pos * 10000^(-2i/c): 0.01 for (c, i) = (44, 11), 10^(-4/3) for (42, 7); other chunks stay put."""
+    p = 5
+    start, width = SPLIT128[axis]
+    i2, f2 = (11, 0.01) if width == 44 else (7, 10.0 ** (-4.0 / 3.0))
+    pos = [np.array([0]), np.array([0]), np.array([0])]
+    pos[axis] = np.array([p])
+    x = np.zeros((1, 128))
+    x[0, start] = 1.0
+    x[0, start + 2 * i2 + 1] = 2.0                       # odd member of pair i2
+    other = SPLIT128[(axis + 1) % 3][0] + 3
+    x[0, other] = 0.7
+    y = A.rope_3d(x, *pos, theta=10000.0)
+    assert y[0, start] == pytest.approx(math.cos(p), abs=1e-15)
+    assert y[0, start + 1] == pytest.approx(math.sin(p), abs=1e-15)
+    assert y[0, start + 2 * i2] == pytest.approx(-2.0 * math.sin(f2 * p), abs=1e-14)
+    assert y[0, start + 2 * i2 + 1] == pytest.approx(2.0 * math.cos(f2 * p), abs=1e-14)
+    assert y[0, other] == 0.7
+    np.testing.assert_array_equal(np.delete(y[0], [start, start + 1, start + 2 * i2, start + 2 * i2 + 1, other]), 0.0)
+
+
+def test_rope128_chunk_boundaries():
+    """A position on one axis moves exactly that axis's channels: [0,44) t, [44,86) h, [86,128) w."""
+    x = np.ones((1, 128))
+    for axis, (start, width) in enumerate(SPLIT128):
+        pos = [np.array([0]), np.array([0]), np.array([0])]
+        pos[axis] = np.array([9])
+        moved = np.nonzero(A.rope_3d(x, *pos, 1e4)[0] != 1.0)[0]
+        assert moved.min() == start and moved.max() == start + width - 1
+
+
+def test_rope128_norms_and_relative_position():
+    a = rng0.standard_normal((30, 128))
+    b = rng0.standard_normal((30, 128))
+    pa = [rng0.integers(0, 50, 30) for _ in range(3)]
+    pb = [rng0.integers(0, 50, 30) for _ in range(3)]
+    ya = A.rope_3d(a, *pa, 1e4)
+    np.testing.assert_allclose(np.hypot(ya[:, 0::2], ya[:, 1::2]), np.hypot(a[:, 0::2], a[:, 1::2]), rtol=1e-14)
+    l0 = np.sum(ya * A.rope_3d(b, *pb, 1e4), axis=1)
+    sh = [4, 13, 2]
+    l1 = np.sum(A.rope_3d(a, *[p + q for p, q in zip(pa, sh)], 1e4)
+                * A.rope_3d(b, *[p + q for p, q in zip(pb, sh)], 1e4), axis=1)
+    np.testing.assert_allclose(l1, l0, rtol=1e-11, atol=1e-11)
+
+
+def test_brute_force_head_dim_128():
+    x = make_inputs("t128")
+    wl = x.workload
+    q, k, v = (np.asarray(t) for t in (x.q, x.k, x.v))
+    o = A.attention(q, k, v, x.wq, x.wk, wl.T, wl.H, wl.W)
+    ob = np.array(B.attention(q.tolist(), k.tolist(), v.tolist(), x.wq, x.wk, wl.T, wl.H, wl.W))
+    assert o.shape == (32, 2, 128)
+    np.testing.assert_allclose(o, ob, rtol=0, atol=1e-12)
+    # scale 1/sqrt(128): logits of a two-token grid with q = k = e_0 (t chunk, t = 0: no rotation)
+    Q = np.zeros((2, 1, 128)); K = np.zeros((2, 1, 128)); V = rng0.standard_normal((2, 1, 128))
+    Q[:, 0, 0] = 1.0; K[0, 0, 0] = 1.0; K[1, 0, 0] = -1.0
+    ones = np.ones(128)
+    o2 = A.attention(Q, K, V, ones, ones, 1, 1, 2, eps=0.0)
+    g = math.sqrt(128.0)                                # |q^| = |k^| = sqrt(128) after the norm
+    lg = np.array([g * g, -g * g]) / math.sqrt(128.0)
+    p = np.exp(lg - lg.max()); p /= p.sum()
+    np.testing.assert_allclose(o2[0, 0], p @ V[:, 0, :], rtol=1e-12)
+
+
+def test_router_head_dim_128_sparse_brute_force():
+    x = make_inputs("s1_128")
+    wl = x.workload
+    m = R.route_mask(x.q, x.k, x.wq, x.wk, wl.T, wl.H, wl.W, 0.5)
+    assert m.shape == (2, 2, 2) and np.all(m.sum(axis=2) == R.keep_count(2, 0.5))
+    q, k, v = (np.asarray(t) for t in (x.q, x.k, x.v))
+    rows = np.array([0, 5, 127, 128, 199])
+    o = A.attention(q, k, v, x.wq, x.wk, wl.T, wl.H, wl.W, rows=rows, mask=m)
+    ob = np.array(B.attention(q.tolist(), k.tolist(), v.tolist(), x.wq, x.wk, wl.T, wl.H, wl.W, mask=m.tolist()))
+    np.testing.assert_allclose(o, ob[rows], rtol=0, atol=1e-12)
