@@ -36,6 +36,9 @@ DESCR = {
              "split by head over 8 GPUs"),
     "j_edit2": ("joint attention, image edit with 2 reference images: 65,536 target queries against "
                 "197,120 keys (512 text + 2 x 65,536 reference + 65,536 target tokens), 56 heads x 96"),
+    "v5d128": ("dense attention at head dim 128, 124,992 tokens, 42 heads x 128 (the same 5376 hidden width; "
+               "RoPE chunks 44/42/42)"),
+    "v5s128": ("route + block-sparse attention (sparsity 0.75) at head dim 128, 124,992 tokens, 42 heads x 128"),
     "b_v5": ("operators around attention at 124,992 tokens, hidden 5376, FFN 14336: AdaLN update, gated "
              "residual + AdaLN update, SwiGLU, gated residual"),
 }
@@ -87,7 +90,7 @@ def bench_joint(args, torch, dit):
     qp = torch.from_numpy(x.q_pos).to(dev)
     kp = torch.from_numpy(x.k_pos).to(dev)
     o = torch.empty_like(q)
-    ws = torch.empty(dit.dit_attn_joint_workspace_bytes(wl.Nq, wl.Nkv, wl.heads, 96, x.max_pos), dtype=torch.uint8,
+    ws = torch.empty(dit.dit_attn_joint_workspace_bytes(wl.Nq, wl.Nkv, wl.heads, wl.head_dim, x.max_pos), dtype=torch.uint8,
                      device=dev)
     stream = torch.cuda.current_stream()
 
@@ -106,18 +109,18 @@ def bench_joint(args, torch, dit):
     torch.cuda.synchronize()
     ms_step = (time.perf_counter() - t0) * 1e3 / args.steps
     ms_call = float(np.mean([e[0].elapsed_time(e[1]) for e in events]))
-    flops = 4.0 * wl.Nq * wl.Nkv * 96 * wl.heads
+    flops = 4.0 * wl.Nq * wl.Nkv * wl.head_dim * wl.heads
     tflops = flops / (ms_step * 1e-3) / 1e12
     result = {
         "metric": METRIC, "value": round(tflops, 2), "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps,
         "warmup": args.warmup, "ms_per_step": round(ms_step, 3), "higher_is_better": True, "scaling": "weak",
         "vs_baseline": None, "dtype": "bf16", "data": "synthetic (seeded N(0,1) bf16 Q/K/V; norm weights 1+0.1N(0,1))",
         "config": {"workload": f"{wl.name}: {DESCR[wl.name]}", "queries": wl.Nq, "keys": wl.Nkv, "heads": wl.heads,
-                   "head_dim": 96, "mode": "joint"},
+                   "head_dim": wl.head_dim, "mode": "joint"},
         "frac_of_bf16_peak": round(tflops / PEAK_BF16_TFLOPS, 4),
         "roofline": {"bound": "mfma", "achieved": round(flops / (ms_call * 1e-3) / 1e12, 2), "peak": PEAK_BF16_TFLOPS,
                      "unit": "TFLOP/s", "frac": round(flops / (ms_call * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4),
-                     "traffic": None, "kernel": "attn_static_kernel<2, false>", "kernel_ms": round(ms_call, 3),
+                     "traffic": None, "kernel": f"attn_static_kernel<{wl.head_dim}, false>", "kernel_ms": round(ms_call, 3),
                      "timed": "whole call: K^/V fragment prepass + attention kernels", "flops_per_launch": flops},
     }
     print(json.dumps(result), flush=True)
@@ -258,7 +261,7 @@ def main():
     sparse = wl.mode == "sparse"
     mask = torch.empty((wl.heads, wl.nb, wl.nb), dtype=torch.uint8, device=dev) if sparse else None
     stream = torch.cuda.current_stream()
-    N, H, d = wl.N, wl.heads, 96
+    N, H, d = wl.N, wl.heads, wl.head_dim
     dense_flops = 4.0 * N * N * d * H
 
     def step(ev=None):
@@ -307,7 +310,7 @@ def main():
 
     if sparse:
         mask_np = mask.cpu().numpy()
-        flops = executed_flops(mask_np, N)
+        flops = executed_flops(mask_np, N, d=d)
     else:
         mask_np = None
         flops = dense_flops
@@ -342,7 +345,7 @@ def main():
         "frac_of_bf16_peak": round(tflops / PEAK_BF16_TFLOPS, 4),
         "roofline": {"bound": "mfma", "achieved": round(attn_tflops, 2), "peak": PEAK_BF16_TFLOPS,
                      "unit": "TFLOP/s", "frac": round(attn_tflops / PEAK_BF16_TFLOPS, 4), "traffic": traffic,
-                     "kernel": "attn_static_kernel<2, " + ("true>" if sparse else "false>"),
+                     "kernel": f"attn_static_kernel<{d}, " + ("true>" if sparse else "false>"),
                      "timed": "whole call: K^/V fragment prepass + attention kernels",
                      "kernel_ms": round(ms_attn, 3), "flops_per_launch": flops},
     }

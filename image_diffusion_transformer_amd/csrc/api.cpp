@@ -38,15 +38,18 @@ size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
 
 struct Shape {
   int T, H, W, heads;
+  int d;             // head dim: 96 or 128
   long long N;
   int nb;
   int nqt;
 };
 
+bool head_dim_ok(int d) { return d == 96 || d == 128; }
+
 struct Layout {
-  size_t tab;        // RoPE table [(T+H+W)][32] f32
-  size_t kvf;        // K^ / V^T fragment images [heads][nb] x 48 KB (dense and block-sparse)
-  size_t route_pool; // [2][heads][nb][96] f32
+  size_t tab;        // RoPE table [(T+H+W)][rope_row_floats(d)] f32
+  size_t kvf;        // K^ / V^T fragment images [heads][nb] x tile_image_bytes(d) (dense and block-sparse)
+  size_t route_pool; // [2][heads][nb][d] f32
   size_t route_score;// [heads][nb][nb] u32 order keys (nb <= dit::route_topk_max_blocks(), else unused)
   size_t list;       // [heads][nqt][nb] i32
   size_t list_len;   // [heads][nqt] i32
@@ -56,9 +59,9 @@ struct Layout {
 Layout make_layout(const Shape& s) {
   Layout L{};
   L.tab = 0;
-  L.kvf = align256((size_t)(s.T + s.H + s.W) * dit::kRopeRow * sizeof(float));
-  const size_t base = L.kvf + (size_t)s.heads * s.nb * dit::kTileImageBytes;
-  const size_t pool_bytes = align256(2ull * s.heads * s.nb * dit::kHeadDim * sizeof(float));
+  L.kvf = align256((size_t)(s.T + s.H + s.W) * dit::rope_row_floats(s.d) * sizeof(float));
+  const size_t base = L.kvf + (size_t)s.heads * s.nb * dit::tile_image_bytes(s.d);
+  const size_t pool_bytes = align256(2ull * s.heads * s.nb * s.d * sizeof(float));
   const size_t score_bytes =
       s.nb <= dit::route_topk_max_blocks() ? align256((size_t)s.heads * s.nb * s.nb * sizeof(uint32_t)) : 0;
   L.route_pool = base;
@@ -77,11 +80,11 @@ bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
 dit_status check_shape(int T, int H, int W, int heads, int head_dim, Shape& s) {
   if (T < 1 || H < 1 || W < 1 || heads < 1)
     return fail(DIT_ERR_INVALID_ARG, "grid and heads must be >= 1 (T=%d H=%d W=%d heads=%d)", T, H, W, heads);
-  if (head_dim != dit::kHeadDim)
-    return fail(DIT_ERR_UNSUPPORTED, "head_dim %d is not supported (only 96)", head_dim);
+  if (!head_dim_ok(head_dim))
+    return fail(DIT_ERR_UNSUPPORTED, "head_dim %d is not supported (96 or 128)", head_dim);
   const long long N = (long long)T * H * W;
-  if (N * heads * dit::kHeadDim > 2147483647ll)
-    return fail(DIT_ERR_UNSUPPORTED, "N*heads*head_dim = %lld exceeds 2^31-1 elements", N * heads * dit::kHeadDim);
+  if (N * heads * head_dim > 2147483647ll)
+    return fail(DIT_ERR_UNSUPPORTED, "N*heads*head_dim = %lld exceeds 2^31-1 elements", N * heads * head_dim);
   const long long nb = (N + dit::kBlock - 1) / dit::kBlock;
   if (nb > 32768) return fail(DIT_ERR_UNSUPPORTED, "%lld blocks exceed the router limit of 32768", nb);
   if ((long long)T + H + W > (1 << 24)) return fail(DIT_ERR_UNSUPPORTED, "grid axes too long");
@@ -89,9 +92,10 @@ dit_status check_shape(int T, int H, int W, int heads, int head_dim, Shape& s) {
   s.H = H;
   s.W = W;
   s.heads = heads;
+  s.d = head_dim;
   s.N = N;
   s.nb = (int)nb;
-  const int bq = dit::attn_query_tile();
+  const int bq = dit::attn_query_tile(head_dim);
   s.nqt = (int)((N + bq - 1) / bq);
   return DIT_OK;
 }
@@ -113,28 +117,32 @@ dit_status check_workspace(const Shape& s, void* ws, size_t ws_bytes, Layout& L)
   return DIT_OK;
 }
 
-// cos / sin of pos * theta^(-2i/32) per axis position, angle in double, C library cos/sin,
-// rounded once to float.  Rows: t in [0,T), then T + h, then T + H + w; each row 16 cos then 16 sin.
+// cos / sin of pos * theta^(-2i/w_a) for the pairs i of axis a (w_a its channel width), angle in
+// double, C library cos/sin, rounded once to float.  Rows: n0 rows of axis 0 (t), then n1 of axis 1 (h),
+// then n2 of axis 2 (w); each row holds the axis's cos values from float 0 and its sin values from
+// float rope_row_floats(d) / 2.
 std::mutex g_tab_mu;
-std::map<std::tuple<int, int, int, uint32_t>, std::vector<float>> g_tabs;
+std::map<std::tuple<int, int, int, uint32_t, int>, std::vector<float>> g_tabs;
 
-const std::vector<float>& rope_table(int T, int H, int W, float theta) {
+const std::vector<float>& rope_table(int n0, int n1, int n2, float theta, int d) {
   uint32_t tb;
   std::memcpy(&tb, &theta, 4);
   std::lock_guard<std::mutex> lk(g_tab_mu);
-  auto key = std::make_tuple(T, H, W, tb);
+  auto key = std::make_tuple(n0, n1, n2, tb, d);
   auto it = g_tabs.find(key);
   if (it != g_tabs.end()) return it->second;
-  std::vector<float> tab((size_t)(T + H + W) * dit::kRopeRow);
-  const int npos[3] = {T, H, W};
+  const int rs = dit::rope_row_floats(d);
+  std::vector<float> tab((size_t)(n0 + n1 + n2) * rs, 0.0f);
+  const int npos[3] = {n0, n1, n2};
   int row = 0;
   for (int a = 0; a < 3; ++a) {
+    const int width = dit::rope_width(d, a);
     for (int p = 0; p < npos[a]; ++p, ++row) {
-      for (int i = 0; i < dit::kPairs; ++i) {
-        const double inv = std::pow((double)theta, -2.0 * i / (double)dit::kAxisDim);
+      for (int i = 0; i < width / 2; ++i) {
+        const double inv = std::pow((double)theta, -2.0 * i / (double)width);
         const double ang = (double)p * inv;
-        tab[(size_t)row * dit::kRopeRow + i] = (float)std::cos(ang);
-        tab[(size_t)row * dit::kRopeRow + dit::kPairs + i] = (float)std::sin(ang);
+        tab[(size_t)row * rs + i] = (float)std::cos(ang);
+        tab[(size_t)row * rs + rs / 2 + i] = (float)std::sin(ang);
       }
     }
   }
@@ -142,7 +150,7 @@ const std::vector<float>& rope_table(int T, int H, int W, float theta) {
 }
 
 dit_status upload_table(const Shape& s, float theta, void* ws, const Layout& L, hipStream_t st) {
-  const std::vector<float>& tab = rope_table(s.T, s.H, s.W, theta);
+  const std::vector<float>& tab = rope_table(s.T, s.H, s.W, theta, s.d);
   hipError_t e = hipMemcpyAsync((char*)ws + L.tab, tab.data(), tab.size() * sizeof(float), hipMemcpyHostToDevice, st);
   if (e != hipSuccess) return fail_hip(e, "hipMemcpyAsync(rope table)");
   return DIT_OK;
@@ -177,7 +185,8 @@ dit::AttnArgs attn_args(const Shape& s, const void* q, const void* k, const void
   a.q_pos = nullptr;
   a.k_pos = nullptr;
   a.max_pos = 0;
-  a.qscale = (float)(1.4426950408889634 / std::sqrt((double)dit::kHeadDim));
+  a.head_dim = s.d;
+  a.qscale = (float)(1.4426950408889634 / std::sqrt((double)s.d));
   a.eps = eps;
   a.nqt = s.nqt;
   a.total = s.heads * s.nqt;
@@ -195,39 +204,42 @@ int keep_count(int nb, float sparsity) {
 constexpr int kMaxPos = 1 << 20;
 
 struct JointShape {
-  int nq, nk, heads, nb, nqt, max_pos;
+  int nq, nk, heads, d, nb, nqt, max_pos;
+  int sections;   // RoPE table sections of max_pos rows: 1 (the axes share one; d = 96) or 3 (d = 128)
 };
 
 struct JointLayout {
-  size_t tab;   // RoPE table [max_pos][32] f32
-  size_t kvf;   // K^ / V^T fragment images [heads][nb] x 48 KB
+  size_t tab;   // RoPE table [sections * max_pos][rope_row_floats(d)] f32
+  size_t kvf;   // K^ / V^T fragment images [heads][nb] x tile_image_bytes(d)
   size_t total;
 };
 
 JointLayout make_joint_layout(const JointShape& j) {
   JointLayout L{};
   L.tab = 0;
-  L.kvf = align256((size_t)j.max_pos * dit::kRopeRow * sizeof(float));
-  L.total = L.kvf + (size_t)j.heads * j.nb * dit::kTileImageBytes;
+  L.kvf = align256((size_t)j.sections * j.max_pos * dit::rope_row_floats(j.d) * sizeof(float));
+  L.total = L.kvf + (size_t)j.heads * j.nb * dit::tile_image_bytes(j.d);
   return L;
 }
 
 dit_status check_joint_shape(int nq, int nk, int heads, int head_dim, int max_pos, JointShape& j) {
   if (nq < 1 || nk < 1 || heads < 1)
     return fail(DIT_ERR_INVALID_ARG, "token counts and heads must be >= 1 (nq=%d nk=%d heads=%d)", nq, nk, heads);
-  if (head_dim != dit::kHeadDim)
-    return fail(DIT_ERR_UNSUPPORTED, "head_dim %d is not supported (only 96)", head_dim);
+  if (!head_dim_ok(head_dim))
+    return fail(DIT_ERR_UNSUPPORTED, "head_dim %d is not supported (96 or 128)", head_dim);
   if (max_pos < 1) return fail(DIT_ERR_INVALID_ARG, "max_pos must be >= 1 (got %d)", max_pos);
   if (max_pos > kMaxPos) return fail(DIT_ERR_UNSUPPORTED, "max_pos %d exceeds %d", max_pos, kMaxPos);
   const long long big = std::max(nq, nk);
-  if (big * heads * dit::kHeadDim > 2147483647ll)
+  if (big * heads * head_dim > 2147483647ll)
     return fail(DIT_ERR_UNSUPPORTED, "tokens*heads*head_dim = %lld exceeds 2^31-1 elements",
-                big * heads * dit::kHeadDim);
+                big * heads * head_dim);
   j.nq = nq;
   j.nk = nk;
   j.heads = heads;
+  j.d = head_dim;
+  j.sections = head_dim == 96 ? 1 : 3;
   j.nb = (nk + dit::kBlock - 1) / dit::kBlock;
-  const int bq = dit::attn_query_tile();
+  const int bq = dit::attn_query_tile(head_dim);
   j.nqt = (nq + bq - 1) / bq;
   j.max_pos = max_pos;
   return DIT_OK;
@@ -300,6 +312,7 @@ dit_status dit_attn_route(const void* q, const void* k, const float* wq, const f
   a.pooled = (float*)((char*)workspace + L.route_pool);
   a.scores = (uint32_t*)((char*)workspace + L.route_score);
   a.mask = mask;
+  a.head_dim = s.d;
   const hipError_t e = dit::launch_route(a, stream);
   if (e != hipSuccess) return fail_hip(e, "router kernel launch");
   return DIT_OK;
@@ -328,7 +341,7 @@ dit_status dit_attn_block_sparse(const void* q, const void* k, const void* v, co
   c.heads = s.heads;
   c.nb = s.nb;
   c.nqt = s.nqt;
-  c.group = dit::attn_query_tile() / dit::kBlock;
+  c.group = dit::attn_query_tile(s.d) / dit::kBlock;
   hipError_t e = dit::launch_compact(c, stream);
   if (e != hipSuccess) return fail_hip(e, "mask compaction launch");
   dit::AttnArgs a = attn_args(s, q, k, v, wq, wk, eps, o, workspace, L);
@@ -367,8 +380,10 @@ dit_status dit_attn_joint(const void* q, const void* k, const void* v, const flo
     return fail(DIT_ERR_WORKSPACE, "workspace has %zu bytes, need %zu", workspace_bytes, L.total);
   if (((uintptr_t)workspace & 255u) != 0) return fail(DIT_ERR_INVALID_ARG, "workspace must be 256-byte aligned");
   hipStream_t stream = (hipStream_t)hip_stream;
-  // rows p = 0 .. max_pos-1: cos / sin of p * theta^(-2i/32), the same for the three axes
-  const std::vector<float>& tab = rope_table(max_pos, 0, 0, rope_theta);
+  // rows p = 0 .. max_pos-1 of each axis section; at head dim 96 the three axes have the same width and
+  // share one section
+  const std::vector<float>& tab = j.sections == 1 ? rope_table(max_pos, 0, 0, rope_theta, j.d)
+                                                  : rope_table(max_pos, max_pos, max_pos, rope_theta, j.d);
   hipError_t e = hipMemcpyAsync((char*)workspace + L.tab, tab.data(), tab.size() * sizeof(float),
                                 hipMemcpyHostToDevice, stream);
   if (e != hipSuccess) return fail_hip(e, "hipMemcpyAsync(rope table)");
@@ -388,7 +403,9 @@ dit_status dit_attn_joint(const void* q, const void* k, const void* v, const flo
   a.q_pos = q_pos;
   a.k_pos = k_pos;
   a.max_pos = max_pos;
-  a.qscale = (float)(1.4426950408889634 / std::sqrt((double)dit::kHeadDim));
+  for (int i = 0; i < 3; ++i) a.rope_sec[i] = j.sections == 1 ? 0 : i * max_pos;
+  a.head_dim = j.d;
+  a.qscale = (float)(1.4426950408889634 / std::sqrt((double)j.d));
   a.eps = eps;
   a.nqt = j.nqt;
   a.total = heads * j.nqt;

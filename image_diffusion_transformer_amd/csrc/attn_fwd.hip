@@ -3,20 +3,24 @@
 // What is computed: the H3 SGLang report (CocoLoop), section on the three
 // acceleration tiers, names QK-RMSNorm with 3D RoPE fused ahead of a long,
 // non-causal attention; its SubBlock-Sparse-Attention paragraph prunes whole KV
-// blocks.  Head shape (56 heads x 96) from the H3-Image spec table, DiT row.
+// blocks.  Head shape (56 heads x 96) from the H3-Image spec table, DiT row; the
+// same kernels are instantiated for head dim 128, the SubBlock precondition named
+// in that report's limits section.
 //
 // Design (the same kernels serve dense and block-sparse):
 //  * A bandwidth-bound prepass normalises and rotates every K row once per layer
-//    and writes K^ and V, per (head, 128-key tile), as a 48 KB image of MFMA
-//    operand fragments (64 lanes x 16 bytes each).  The attention kernel then
-//    stages a KV tile with 48 plain global->LDS copies and no vector ALU work,
-//    which leaves the VALU to the softmax.
+//    and writes K^ and V, per (head, 128-key tile), as an image of MFMA operand
+//    fragments (64 lanes x 16 bytes each; 48 KB at head dim 96, 64 KB at 128).
+//    The attention kernel then stages a KV tile with plain global->LDS copies and
+//    no vector ALU work, which leaves the VALU to the softmax.
 //  * Attention work is split per (head, query tile of NW*QB*32 tokens); the launch
 //    index is remapped so the workgroups resident on one XCD walk the same head's
 //    K/V and share its L2.
-//  * Each wave owns QB blocks of 32 queries.  Its Q rows are loaded once (two
-//    lanes per query, 48 channels each), RMS-normalised, rotated, scaled by
-//    log2(e)/sqrt(96) and kept in registers as bf16 MFMA B operands.
+//  * Each wave owns QB blocks of 32 queries (2 at head dim 96, 1 at 128, where
+//    the Q fragments and O accumulators of two blocks would not fit the 256
+//    registers of a wave).  Its Q rows are loaded once (two lanes per query, half
+//    the channels each), RMS-normalised, rotated, scaled by log2(e)/sqrt(d) and
+//    kept in registers as bf16 MFMA B operands.
 //  * KV tiles are double-buffered in LDS: the next tile's fragment image is in
 //    flight (global->LDS, no registers) while the current one is consumed.
 //  * S^T = K^ Q^T with v_mfma_f32_32x32x16_bf16 (keys on rows, queries on columns):
@@ -55,30 +59,31 @@ typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 constexpr int BK = kBlock;    // keys per KV tile (= router block)
 constexpr float kTau = 8.0f;  // lazy-rescale threshold, base-2 log units
 
-// Fragment image of one (head, 128-key tile), written by kv_prep_kernel: 48 fragments of 512 bf16
-// (lane l owns elements 8l..8l+7).
-//   fragment kb*6 + ks        (K^, 0..23):  lane l holds K^[32kb + l%32][16ks + 8(l/32) + e], e = 0..7:
+// Fragment image of one (head, 128-key tile), written by kv_prep_kernel: FRAGS fragments of 512 bf16
+// (lane l owns elements 8l..8l+7).  With KS = d/16 channel steps and DB = d/32 channel blocks:
+//   fragment kb*KS + ks      (K^, 0..4KS-1):  lane l holds K^[32kb + l%32][16ks + 8(l/32) + e], e = 0..7:
 //                             the A operand of S^T for key sub-block kb, channel step ks.
-//   fragment 24 + (2kb+s)*3 + db (V^T, 24..47): lane l holds V[key][32db + l%32] for the keys
+//   fragment 4KS + (2kb+s)*DB + db (V^T):  lane l holds V[key][32db + l%32] for the keys
 //                             32kb + 16s + 4(l/32) + {0, 1, 2, 3, 8, 9, 10, 11}: the A operand of
 //                             O^T for channel block db, k-step s of sub-block kb.  That key order is
 //                             the one in which the S^T accumulator holds the probabilities.
-// Keys past the grid have zero K^ and V.
+// Keys past the grid have zero K^ and V.  Head dim 96: 24 + 24 fragments (48 KB); 128: 32 + 32 (64 KB).
 constexpr int kFrag = 512;
-constexpr int kVFrag0 = 24;
-constexpr int kTileFrags = 48;
-constexpr int kTileElems = kTileFrags * kFrag;   // 24576 bf16 = 48 KB
+constexpr int kNW = 8;   // waves per attention workgroup (2 per SIMD)
 
-// Kernel shape: kNW waves per workgroup, kQB blocks of 32 queries per wave.
-#ifndef DIT_ATTN_NW
-#define DIT_ATTN_NW 8
-#endif
-#ifndef DIT_ATTN_QB
-#define DIT_ATTN_QB 2
-#endif
-constexpr int kNW = DIT_ATTN_NW;
-constexpr int kQB = DIT_ATTN_QB;
-constexpr int kBQ = kNW * kQB * 32;   // queries per workgroup
+template <int D>
+struct Head {
+  static_assert(D == 96 || D == 128, "head dim");
+  static constexpr int KS = D / 16;
+  static constexpr int DB = D / 32;
+  static constexpr int VFRAG0 = 4 * KS;
+  static constexpr int FRAGS = 4 * KS + 8 * DB;
+  static constexpr int TILE = FRAGS * kFrag;         // bf16 elements of one tile image
+  static constexpr int QB = D == 96 ? 2 : 1;          // 32-query blocks per wave
+  static constexpr int BQ = kNW * QB * 32;            // queries per workgroup
+  static constexpr int RS = rope_row_floats(D);       // floats per RoPE table row
+  static constexpr int PAIRS0 = rope_width(D, 0) / 2, PAIRS1 = rope_width(D, 1) / 2;
+};
 
 __device__ __forceinline__ uint32_t fastdiv(uint32_t n, const FastDiv& f) {
   return (uint32_t)(((uint64_t)n * f.m) >> f.s);
@@ -111,12 +116,12 @@ __device__ __forceinline__ float pair_sum(float x) {
 
 // Rows of the RoPE table that rotate the three axis chunks of token n.  Grid tokens: rows t, T + h and
 // T + H + w of the per-axis table.  Tokens with explicit (t, h, w) positions: the coordinates themselves,
-// in one table of max_pos rows that serves all three axes (its rows depend only on the position);
-// coordinates outside [0, max_pos) are clamped to it.
+// clamped to [0, max_pos), in the axis's section of max_pos rows (rope_sec; at head dim 96 the three
+// axes share one section, their rows depending only on the position).
 __device__ __forceinline__ void rope_rows(const AttnArgs& a, const int* pos, int n, int (&r)[3]) {
   if (pos != nullptr) {
 #pragma unroll
-    for (int i = 0; i < 3; ++i) r[i] = min(max(pos[3 * (size_t)n + i], 0), a.max_pos - 1);
+    for (int i = 0; i < 3; ++i) r[i] = a.rope_sec[i] + min(max(pos[3 * (size_t)n + i], 0), a.max_pos - 1);
   } else {
     int t, h, w;
     grid_pos((uint32_t)n, a.g, t, h, w);
@@ -126,14 +131,37 @@ __device__ __forceinline__ void rope_rows(const AttnArgs& a, const int* pos, int
   }
 }
 
-// RMS-normalise (scale r) and rotate 8 consecutive channels 8c..8c+7 held as bf16 in `raw`.
-__device__ __forceinline__ u32x4 norm_rope_chunk(u32x4 raw, float r, float scale, const float* rope_row_ptr,
+// RMS-normalise (scale r) and rotate 8 consecutive channels 8c..8c+7 held as bf16 in `raw`.  rows[a]
+// points at the RoPE table row of axis a for this token (cos of pair i at i, sin at RS/2 + i).
+template <int D>
+__device__ __forceinline__ u32x4 norm_rope_chunk(u32x4 raw, float r, float scale, const float* const (&rows)[3],
                                                  int c, const float* wvec) {
-  const f32x4 co = *(const f32x4*)(rope_row_ptr + 4 * (c & 3));
-  const f32x4 si = *(const f32x4*)(rope_row_ptr + kPairs + 4 * (c & 3));
   const f32x4 w0 = *(const f32x4*)(wvec + 8 * c);
   const f32x4 w1 = *(const f32x4*)(wvec + 8 * c + 4);
   const float wv[8] = {w0[0], w0[1], w0[2], w0[3], w1[0], w1[1], w1[2], w1[3]};
+  float co[4], si[4];
+  if constexpr (D == 96) {
+    // 32-channel axis chunks: the vector's 4 pairs are pairs 4(c%4) .. 4(c%4)+3 of axis c/4
+    const float* rp = rows[c >> 2];
+    const f32x4 cv = *(const f32x4*)(rp + 4 * (c & 3));
+    const f32x4 sv = *(const f32x4*)(rp + Head<D>::RS / 2 + 4 * (c & 3));
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      co[e] = cv[e];
+      si[e] = sv[e];
+    }
+  } else {
+    // chunks of 44, 42, 42 channels: a vector may straddle two axes, so each pair finds its own
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const int p = 4 * c + e;
+      const int ax = (p >= Head<D>::PAIRS0) + (p >= Head<D>::PAIRS0 + Head<D>::PAIRS1);
+      const int i = p - (ax == 0 ? 0 : (ax == 1 ? Head<D>::PAIRS0 : Head<D>::PAIRS0 + Head<D>::PAIRS1));
+      const float* rp = ax == 0 ? rows[0] : (ax == 1 ? rows[1] : rows[2]);
+      co[e] = rp[i];
+      si[e] = rp[Head<D>::RS / 2 + i];
+    }
+  }
   u32x4 out;
 #pragma unroll
   for (int e = 0; e < 4; ++e) {
@@ -146,16 +174,17 @@ __device__ __forceinline__ u32x4 norm_rope_chunk(u32x4 raw, float r, float scale
   return out;
 }
 
-// Softmax modes.  QK-RMSNorm bounds every logit: |q^ . k^| / sqrt(96) <= sqrt(96) max|w_q| max|w_k|
+// Softmax modes.  QK-RMSNorm bounds every logit: |q^ . k^| / sqrt(d) <= sqrt(d) max|w_q| max|w_k|
 // (RoPE preserves norms).  When that bound, in base-2 units, is at most kStaticBound, exp2(S) with
 // no shift can neither overflow nor underflow for any input, and the shift cancels in O / rowsum:
 // no running max, no subtraction, no rescale.  Otherwise the online (running-max) softmax runs.
 enum SoftmaxMode { kStatic = 0, kOnline = 1 };
 constexpr float kStaticBound = 48.0f;
 
+template <int D>
 __device__ __forceinline__ bool static_bound_holds(const AttnArgs& a, int lane) {
   float mq = 0.f, mk = 0.f;
-  for (int i = lane; i < kHeadDim; i += 64) {
+  for (int i = lane; i < D; i += 64) {
     mq = fmaxf(mq, fabsf(a.wq[i]));
     mk = fmaxf(mk, fabsf(a.wk[i]));
   }
@@ -164,22 +193,23 @@ __device__ __forceinline__ bool static_bound_holds(const AttnArgs& a, int lane) 
     mq = fmaxf(mq, __shfl_xor(mq, o));
     mk = fmaxf(mk, __shfl_xor(mk, o));
   }
-  // |q^|, |k^| <= sqrt(96) max|w| (RMS <= 1 after the norm); 1.02 covers rsq, rotation and bf16 rounding.
-  const float bound = 1.4426950408889634f * 9.797958971132712f * mq * mk * 1.02f;
+  // |q^|, |k^| <= sqrt(d) max|w| (RMS <= 1 after the norm); 1.02 covers rsq, rotation and bf16 rounding.
+  const float sqrt_d = D == 96 ? 9.797958971132712f : 11.313708498984761f;
+  const float bound = 1.4426950408889634f * sqrt_d * mq * mk * 1.02f;
   return bound <= kStaticBound;   // false for NaN weights
 }
 
-// Q fragments of the wave: load, RMSNorm, RoPE, scale by log2(e)/sqrt(96), pack to bf16 (once per query).
 // Query block (32 queries) of the workgroup's tile that block qb of a wave holds.  Dense: wave w holds
 // blocks QB*w .. QB*w+QB-1.  Block-sparse (QB = 2): wave w holds part w%4 of router blocks 2(w/4) and
 // 2(w/4)+1, so each router block's 128 queries are spread over all four SIMDs (waves w and w+4 share
 // SIMD w%4) and a KV tile kept by few router blocks still keeps every SIMD busy.
 template <int QB, bool SPARSE>
 __device__ __forceinline__ int query_block(int wave, int qb) {
-  if constexpr (SPARSE) {
-    static_assert(QB == 2, "sparse mapping assumes 2 blocks per wave");
+  if constexpr (SPARSE && QB == 2) {
     return 8 * (wave >> 2) + 4 * qb + (wave & 3);
   } else {
+    // (block-sparse with one block per wave: waves 0-3 and 4-7 hold the two router blocks of the
+    // 256-query tile, each spread over the four SIMDs already)
     return wave * QB + qb;
   }
 }
@@ -189,50 +219,54 @@ __device__ __forceinline__ int router_block(int wave, int qb) {
   return query_block<QB, SPARSE>(wave, qb) >> 2;
 }
 
-template <int QB, int BQ, bool SPARSE>
+// Q fragments of the wave: load, RMSNorm, RoPE, scale by log2(e)/sqrt(d), pack to bf16 (once per query).
+template <int D, int QB, int BQ, bool SPARSE>
 __device__ __forceinline__ void load_q(const AttnArgs& a, int head, int qt, int wave, int lane,
-                                       bf16x8 (&qf)[QB][6]) {
+                                       bf16x8 (&qf)[QB][Head<D>::KS]) {
+  constexpr int KS = Head<D>::KS;
   const int half = lane >> 5, l32 = lane & 31;
 #pragma unroll
   for (int qb = 0; qb < QB; ++qb) {
     const int n = qt * BQ + query_block<QB, SPARSE>(wave, qb) * 32 + l32;
     const bool live = n < a.nq;
-    u32x4 raw[6];
-    const size_t base = ((size_t)(live ? n : 0) * a.g.heads + head) * kHeadDim;
+    u32x4 raw[KS];
+    const size_t base = ((size_t)(live ? n : 0) * a.g.heads + head) * D;
 #pragma unroll
-    for (int ks = 0; ks < 6; ++ks)
+    for (int ks = 0; ks < KS; ++ks)
       raw[ks] = live ? *(const u32x4*)(a.q + base + 16 * ks + 8 * half) : u32x4{0, 0, 0, 0};
     float ss = 0.f;
 #pragma unroll
-    for (int ks = 0; ks < 6; ++ks)
+    for (int ks = 0; ks < KS; ++ks)
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
         const float lo = bf_lo(raw[ks][e]), hi = bf_hi(raw[ks][e]);
         ss += lo * lo + hi * hi;
       }
     ss = pair_sum(ss);
-    const float r = live ? __builtin_amdgcn_rsqf(ss * (1.0f / kHeadDim) + a.eps) : 0.f;
+    const float r = live ? __builtin_amdgcn_rsqf(ss * (1.0f / D) + a.eps) : 0.f;
     int rr[3] = {0, 0, 0};
     if (live) rope_rows(a, a.q_pos, n, rr);
+    const float* const rows[3] = {a.rope + rr[0] * Head<D>::RS, a.rope + rr[1] * Head<D>::RS,
+                                  a.rope + rr[2] * Head<D>::RS};
 #pragma unroll
-    for (int ks = 0; ks < 6; ++ks) {
+    for (int ks = 0; ks < KS; ++ks) {
       const int c = 2 * ks + half;
-      const float* rp = a.rope + rr[ks >> 1] * kRopeRow;
-      qf[qb][ks] = __builtin_bit_cast(bf16x8, norm_rope_chunk(raw[ks], r, a.qscale, rp, c, a.wq));
+      qf[qb][ks] = __builtin_bit_cast(bf16x8, norm_rope_chunk<D>(raw[ks], r, a.qscale, rows, c, a.wq));
     }
   }
 }
 
-// S^T for key sub-block kb (32 keys) against the wave's QB query blocks: 6 K^ fragments, 6*QB MFMAs.
+// S^T for key sub-block kb (32 keys) against the wave's QB query blocks: KS K^ fragments, KS*QB MFMAs.
 // QM: bit qb set = query block qb takes part (block-sparse tiles kept by only some of a wave's blocks).
-template <int QB, int QM = (1 << QB) - 1>
-__device__ __forceinline__ void qk_block(const uint16_t* T_, int kb, int lane, const bf16x8 (&qf)[QB][6],
-                                         f32x16 (&S)[QB]) {
+template <int D, int QB, int QM = (1 << QB) - 1>
+__device__ __forceinline__ void qk_block(const uint16_t* T_, int kb, int lane,
+                                         const bf16x8 (&qf)[QB][Head<D>::KS], f32x16 (&S)[QB]) {
+  constexpr int KS = Head<D>::KS;
 #pragma unroll
   for (int qb = 0; qb < QB; ++qb) S[qb] = f32x16{};
 #pragma unroll
-  for (int ks = 0; ks < 6; ++ks) {
-    const bf16x8 ka = *(const bf16x8*)(T_ + (kb * 6 + ks) * kFrag + lane * 8);
+  for (int ks = 0; ks < KS; ++ks) {
+    const bf16x8 ka = *(const bf16x8*)(T_ + (kb * KS + ks) * kFrag + lane * 8);
 #pragma unroll
     for (int qb = 0; qb < QB; ++qb)
       if (((QM >> qb) & 1) != 0)
@@ -240,15 +274,16 @@ __device__ __forceinline__ void qk_block(const uint16_t* T_, int kb, int lane, c
   }
 }
 
-// O^T += V^T P^T for key sub-block kb: 6 V^T fragments, 6*QB MFMAs.
-template <int QB, int QM = (1 << QB) - 1>
+// O^T += V^T P^T for key sub-block kb: 2*DB V^T fragments, 2*DB*QB MFMAs.
+template <int D, int QB, int QM = (1 << QB) - 1>
 __device__ __forceinline__ void pv_block(const uint16_t* T_, int kb, int lane, const bf16x8 (&P)[QB][2],
-                                         f32x16 (&acc)[QB][3]) {
+                                         f32x16 (&acc)[QB][Head<D>::DB]) {
+  constexpr int DB = Head<D>::DB;
 #pragma unroll
   for (int s = 0; s < 2; ++s)
 #pragma unroll
-    for (int db = 0; db < 3; ++db) {
-      const bf16x8 va = *(const bf16x8*)(T_ + (kVFrag0 + (2 * kb + s) * 3 + db) * kFrag + lane * 8);
+    for (int db = 0; db < DB; ++db) {
+      const bf16x8 va = *(const bf16x8*)(T_ + (Head<D>::VFRAG0 + (2 * kb + s) * DB + db) * kFrag + lane * 8);
 #pragma unroll
       for (int qb = 0; qb < QB; ++qb)
         if (((QM >> qb) & 1) != 0)
@@ -278,9 +313,9 @@ __device__ __forceinline__ bool key_live(int key0, int i, int half, int N) {
 }
 
 // Online (running-max) softmax of one sub-block; keys >= N get probability 0.
-template <int QB, int QM = (1 << QB) - 1>
+template <int DB, int QB, int QM = (1 << QB) - 1>
 __device__ __forceinline__ void softmax_online(f32x16 (&S)[QB], bool ragged, int key0, int N, int lane,
-                                               float (&m)[QB], float (&l)[QB], f32x16 (&acc)[QB][3],
+                                               float (&m)[QB], float (&l)[QB], f32x16 (&acc)[QB][DB],
                                                bf16x8 (&P)[QB][2]) {
   const int half = lane >> 5;
   if (ragged) {
@@ -303,7 +338,7 @@ __device__ __forceinline__ void softmax_online(f32x16 (&S)[QB], bool ragged, int
       const float alpha = __builtin_amdgcn_exp2f(m[qb] - mn);
       l[qb] *= alpha;
 #pragma unroll
-      for (int db = 0; db < 3; ++db) acc[qb][db] *= alpha;
+      for (int db = 0; db < DB; ++db) acc[qb][db] *= alpha;
       m[qb] = mn;
     }
     float p[16];
@@ -327,9 +362,9 @@ __device__ __forceinline__ void softmax_static(const f32x16 (&S)[QB], float (&l)
   }
 }
 
-template <int QB, int BQ, bool SPARSE>
+template <int D, int QB, int BQ, bool SPARSE>
 __device__ __forceinline__ void store_o(const AttnArgs& a, int head, int qt, int wave, int lane,
-                                        const f32x16 (&acc)[QB][3], const float (&l)[QB]) {
+                                        const f32x16 (&acc)[QB][Head<D>::DB], const float (&l)[QB]) {
   const int half = lane >> 5, l32 = lane & 31;
 #pragma unroll
   for (int qb = 0; qb < QB; ++qb) {
@@ -337,9 +372,9 @@ __device__ __forceinline__ void store_o(const AttnArgs& a, int head, int qt, int
     const float lt = pair_sum(l[qb]);
     const float inv = lt > 0.f ? 1.0f / lt : 0.f;
     if (n < a.nq) {
-      uint16_t* op = a.o + ((size_t)n * a.g.heads + head) * kHeadDim;
+      uint16_t* op = a.o + ((size_t)n * a.g.heads + head) * D;
 #pragma unroll
-      for (int db = 0; db < 3; ++db)
+      for (int db = 0; db < Head<D>::DB; ++db)
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
           const int d = db * 32 + 8 * j + 4 * half;
@@ -379,36 +414,38 @@ __device__ __forceinline__ bool tile_iter(const AttnArgs& a, TileIter& ti) {
 // ------------------------------------------------------------------------------------------------
 // K^ / V fragment prepass: one workgroup per (128-key tile, head).  The tile's raw K and V rows are read
 // with coalesced 16-byte loads into LDS; each K row is RMS-normalised and rotated (two threads per row,
-// six 8-channel chunks each) and every fragment lane slot is written with one 16-byte store.
+// d/16 8-channel chunks each) and every fragment lane slot is written with one 16-byte store.
+template <int D>
 __global__ void __launch_bounds__(256) kv_prep_kernel(AttnArgs a) {
-  __shared__ __attribute__((aligned(16))) uint16_t rk[BK * kHeadDim];
-  __shared__ __attribute__((aligned(16))) uint16_t rv[BK * kHeadDim];
-  __shared__ __attribute__((aligned(16))) float sW[kHeadDim];
+  constexpr int KS = Head<D>::KS, DB = Head<D>::DB, CH = D / 8;
+  __shared__ __attribute__((aligned(16))) uint16_t rk[BK * D];
+  __shared__ __attribute__((aligned(16))) uint16_t rv[BK * D];
+  __shared__ __attribute__((aligned(16))) float sW[D];
   const int tile = blockIdx.x, head = blockIdx.y, tid = threadIdx.x;
   const int N = a.nk;
-  if (tid < kHeadDim) sW[tid] = a.wk[tid];
-  for (int i = tid; i < BK * 12; i += 256) {
-    const int row = i / 12, c = i - 12 * row;
+  if (tid < D) sW[tid] = a.wk[tid];
+  for (int i = tid; i < BK * CH; i += 256) {
+    const int row = i / CH, c = i - CH * row;
     const int n = tile * BK + row;
     u32x4 kx = {0, 0, 0, 0}, vx = {0, 0, 0, 0};
     if (n < N) {
-      const size_t off = ((size_t)n * a.g.heads + head) * kHeadDim + 8 * c;
+      const size_t off = ((size_t)n * a.g.heads + head) * D + 8 * c;
       kx = *(const u32x4*)(a.k + off);
       vx = *(const u32x4*)(a.v + off);
     }
-    *(u32x4*)(rk + row * kHeadDim + 8 * c) = kx;
-    *(u32x4*)(rv + row * kHeadDim + 8 * c) = vx;
+    *(u32x4*)(rk + row * D + 8 * c) = kx;
+    *(u32x4*)(rv + row * D + 8 * c) = vx;
   }
   __syncthreads();
-  uint16_t* img = a.kvf + ((size_t)head * a.nb + tile) * kTileElems;
+  uint16_t* img = a.kvf + ((size_t)head * a.nb + tile) * Head<D>::TILE;
   {
-    const int kk = tid & (BK - 1), cg = tid >> 7;     // key row; chunks 6cg .. 6cg+5
+    const int kk = tid & (BK - 1), cg = tid >> 7;     // key row; chunks KS*cg .. KS*cg + KS-1
     const int n = tile * BK + kk;
     const bool live = n < N;
-    const u32x4* row = (const u32x4*)(rk + kk * kHeadDim);
+    const u32x4* row = (const u32x4*)(rk + kk * D);
     float ss = 0.f;
 #pragma unroll
-    for (int c = 0; c < 12; ++c) {
+    for (int c = 0; c < CH; ++c) {
       const u32x4 x = row[c];
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
@@ -416,39 +453,44 @@ __global__ void __launch_bounds__(256) kv_prep_kernel(AttnArgs a) {
         ss += lo * lo + hi * hi;
       }
     }
-    const float r = live ? __builtin_amdgcn_rsqf(ss * (1.0f / kHeadDim) + a.eps) : 0.f;
+    const float r = live ? __builtin_amdgcn_rsqf(ss * (1.0f / D) + a.eps) : 0.f;
     int rr[3] = {0, 0, 0};
     if (live) rope_rows(a, a.k_pos, n, rr);
+    const float* const rows[3] = {a.rope + rr[0] * Head<D>::RS, a.rope + rr[1] * Head<D>::RS,
+                                  a.rope + rr[2] * Head<D>::RS};
 #pragma unroll
-    for (int j = 0; j < 6; ++j) {
-      const int c = 6 * cg + j;                        // channels 8c .. 8c+7 = step c/2, lane half c%2
-      const float* rp = a.rope + rr[c >> 2] * kRopeRow;
-      const u32x4 y = norm_rope_chunk(row[c], r, 1.0f, rp, c, sW);
-      *(u32x4*)(img + ((kk >> 5) * 6 + (c >> 1)) * kFrag + ((c & 1) * 32 + (kk & 31)) * 8) =
+    for (int j = 0; j < KS; ++j) {
+      const int c = KS * cg + j;                       // channels 8c .. 8c+7 = step c/2, lane half c%2
+      const u32x4 y = norm_rope_chunk<D>(row[c], r, 1.0f, rows, c, sW);
+      *(u32x4*)(img + ((kk >> 5) * KS + (c >> 1)) * kFrag + ((c & 1) * 32 + (kk & 31)) * 8) =
           live ? y : u32x4{0, 0, 0, 0};
     }
   }
-  for (int i = tid; i < (kTileFrags - kVFrag0) * 64; i += 256) {
-    const int f = i >> 6, l = i & 63;                  // f = (2kb + s)*3 + db
-    const int d = 32 * (f % 3) + (l & 31);
-    const int key0 = 16 * (f / 3) + 4 * (l >> 5);
+  for (int i = tid; i < 8 * DB * 64; i += 256) {
+    const int f = i >> 6, l = i & 63;                  // f = (2kb + s)*DB + db
+    const int d = 32 * (f % DB) + (l & 31);
+    const int key0 = 16 * (f / DB) + 4 * (l >> 5);
     uint32_t w[4];
 #pragma unroll
     for (int e2 = 0; e2 < 4; ++e2) {
       const int key = key0 + 2 * e2 + (e2 >= 2 ? 4 : 0);
-      w[e2] = (uint32_t)rv[key * kHeadDim + d] | ((uint32_t)rv[(key + 1) * kHeadDim + d] << 16);
+      w[e2] = (uint32_t)rv[key * D + d] | ((uint32_t)rv[(key + 1) * D + d] << 16);
     }
-    *(u32x4*)(img + (kVFrag0 + f) * kFrag + l * 8) = u32x4{w[0], w[1], w[2], w[3]};
+    *(u32x4*)(img + (Head<D>::VFRAG0 + f) * kFrag + l * 8) = u32x4{w[0], w[1], w[2], w[3]};
   }
 }
 
-// This wave's share (fragments 6w .. 6w+5) of one tile's fragment image, copied global -> LDS without
-// passing through registers: lane l of each copy moves the 16 bytes of lane slot l.
+// This wave's share (fragments FPW*w .. FPW*w + FPW-1, FPW = FRAGS / 8) of one tile's fragment image,
+// copied global -> LDS without passing through registers: lane l of each copy moves the 16 bytes of lane
+// slot l.
+template <int D>
 __device__ __forceinline__ void dma_tile(const uint16_t* src, int wave, int lane, uint16_t* dst) {
   typedef __attribute__((address_space(3))) void lds_void;
+  constexpr int FPW = Head<D>::FRAGS / kNW;
+  static_assert(FPW * kNW == Head<D>::FRAGS, "fragments per wave");
 #pragma unroll
-  for (int c = 0; c < 6; ++c) {
-    const int f = 6 * wave + c;
+  for (int c = 0; c < FPW; ++c) {
+    const int f = FPW * wave + c;
     __builtin_amdgcn_global_load_lds((const void*)(src + f * kFrag + lane * 8), (lds_void*)(dst + f * kFrag), 16,
                                      0, 0);
   }
@@ -471,44 +513,45 @@ __device__ __forceinline__ void tile_barrier() {
 // Attention kernels: 8 waves (2 per SIMD), QB blocks of 32 queries per wave.  Per KV tile: start the copy
 // of the next tile's fragment image into the other LDS stage, then per 32-key sub-block: S MFMAs, softmax,
 // PV MFMAs.  One barrier per tile.  Block-sparse tiles are computed only for the query blocks whose
-// router block keeps them (activity mask QM of the wave's two blocks).
-template <int QB, int QM, int MODE>
-__device__ __forceinline__ void tile_body(const uint16_t* T_, int lane, const bf16x8 (&qf)[QB][6],
-                                          f32x16 (&acc)[QB][3], float (&m)[QB], float (&l)[QB], bool ragged,
-                                          int key0, int N) {
+// router block keeps them (activity mask QM of the wave's blocks).
+template <int D, int QB, int QM, int MODE>
+__device__ __forceinline__ void tile_body(const uint16_t* T_, int lane, const bf16x8 (&qf)[QB][Head<D>::KS],
+                                          f32x16 (&acc)[QB][Head<D>::DB], float (&m)[QB], float (&l)[QB],
+                                          bool ragged, int key0, int N) {
 #pragma unroll 1
   for (int kb = 0; kb < BK / 32; ++kb) {
     f32x16 S[QB];
-    qk_block<QB, QM>(T_, kb, lane, qf, S);
+    qk_block<D, QB, QM>(T_, kb, lane, qf, S);
     bf16x8 P[QB][2];
     if constexpr (MODE == kStatic)
       softmax_static<QB, QM>(S, l, P);
     else
-      softmax_online<QB, QM>(S, ragged, key0 + kb * 32, N, lane, m, l, acc, P);
-    pv_block<QB, QM>(T_, kb, lane, P, acc);
+      softmax_online<Head<D>::DB, QB, QM>(S, ragged, key0 + kb * 32, N, lane, m, l, acc, P);
+    pv_block<D, QB, QM>(T_, kb, lane, P, acc);
   }
 }
 
 // Static mode: keys past the grid have zero K^ and V: S = 0 and p = 1 there, they add nothing to O and
 // their count is taken off the row sum at the end -- no masking inside the loop.  Online mode (for norm
 // weights whose logit bound is too large for the static shift) masks them.
-template <int QB, bool SPARSE, int MODE>
+template <int D, bool SPARSE, int MODE>
 __device__ __forceinline__ void attn_kernel_body(const AttnArgs& a, uint16_t* sKV) {
-  constexpr int NW = 8, BQ = NW * QB * 32;
-  static_assert(NW * 6 == kTileFrags && BQ % BK == 0, "tile shape");
+  constexpr int QB = Head<D>::QB, BQ = Head<D>::BQ, TILE = Head<D>::TILE;
+  constexpr int KS = Head<D>::KS, DB = Head<D>::DB;
+  static_assert(BQ % BK == 0, "tile shape");
   TileIter ti;
   if (!tile_iter<SPARSE>(a, ti)) return;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  if (static_bound_holds(a, lane) != (MODE == kStatic)) return;   // the other kernel handles these weights
+  if (static_bound_holds<D>(a, lane) != (MODE == kStatic)) return;   // the other kernel handles these weights
   const int N = a.nk, nt = ti.ntiles;
   int rbit[QB];
 #pragma unroll
   for (int qb = 0; qb < QB; ++qb) rbit[qb] = router_block<QB, SPARSE>(wave, qb);
-  const uint16_t* img = a.kvf + (size_t)ti.head * a.nb * kTileElems;
-  if (nt > 0) dma_tile(img + (size_t)ti.tile(0, SPARSE) * kTileElems, wave, lane, sKV);
-  bf16x8 qf[QB][6];
-  load_q<QB, BQ, SPARSE>(a, ti.head, ti.qt, wave, lane, qf);
-  f32x16 acc[QB][3];
+  const uint16_t* img = a.kvf + (size_t)ti.head * a.nb * TILE;
+  if (nt > 0) dma_tile<D>(img + (size_t)ti.tile(0, SPARSE) * TILE, wave, lane, sKV);
+  bf16x8 qf[QB][KS];
+  load_q<D, QB, BQ, SPARSE>(a, ti.head, ti.qt, wave, lane, qf);
+  f32x16 acc[QB][DB];
   float m[QB], l[QB];
   int pad[QB];                                     // static mode: keys past the grid counted in l
 #pragma unroll
@@ -517,28 +560,30 @@ __device__ __forceinline__ void attn_kernel_body(const AttnArgs& a, uint16_t* sK
     l[qb] = 0.f;
     pad[qb] = 0;
 #pragma unroll
-    for (int db = 0; db < 3; ++db) acc[qb][db] = f32x16{};
+    for (int db = 0; db < DB; ++db) acc[qb][db] = f32x16{};
   }
   tile_barrier();
   for (int it = 0; it < nt; ++it) {
     const int st = it & 1, tile = ti.tile(it, SPARSE);
     if (it + 1 < nt)
-      dma_tile(img + (size_t)ti.tile(it + 1, SPARSE) * kTileElems, wave, lane, sKV + (st ^ 1) * kTileElems);
+      dma_tile<D>(img + (size_t)ti.tile(it + 1, SPARSE) * TILE, wave, lane, sKV + (st ^ 1) * TILE);
     const int flags = ti.flags(it, SPARSE);
     int qm = 0;
 #pragma unroll
     for (int qb = 0; qb < QB; ++qb) qm |= ((flags >> rbit[qb]) & 1) << qb;
-    const uint16_t* T_ = sKV + st * kTileElems;
+    const uint16_t* T_ = sKV + st * TILE;
     const bool ragged = (tile + 1) * BK > N;
     if constexpr (SPARSE && QB == 2) {
       if (qm == 3)
-        tile_body<QB, 3, MODE>(T_, lane, qf, acc, m, l, ragged, tile * BK, N);
+        tile_body<D, QB, 3, MODE>(T_, lane, qf, acc, m, l, ragged, tile * BK, N);
       else if (qm == 1)
-        tile_body<QB, 1, MODE>(T_, lane, qf, acc, m, l, ragged, tile * BK, N);
+        tile_body<D, QB, 1, MODE>(T_, lane, qf, acc, m, l, ragged, tile * BK, N);
       else if (qm == 2)
-        tile_body<QB, 2, MODE>(T_, lane, qf, acc, m, l, ragged, tile * BK, N);
+        tile_body<D, QB, 2, MODE>(T_, lane, qf, acc, m, l, ragged, tile * BK, N);
+    } else if constexpr (SPARSE) {
+      if (qm != 0) tile_body<D, QB, (1 << QB) - 1, MODE>(T_, lane, qf, acc, m, l, ragged, tile * BK, N);
     } else {
-      tile_body<QB, (1 << QB) - 1, MODE>(T_, lane, qf, acc, m, l, ragged, tile * BK, N);
+      tile_body<D, QB, (1 << QB) - 1, MODE>(T_, lane, qf, acc, m, l, ragged, tile * BK, N);
     }
     if constexpr (MODE == kStatic) {
 #pragma unroll
@@ -551,19 +596,19 @@ __device__ __forceinline__ void attn_kernel_body(const AttnArgs& a, uint16_t* sK
 #pragma unroll
     for (int qb = 0; qb < QB; ++qb) l[qb] -= (lane < 32) ? (float)pad[qb] : 0.f;
   }
-  store_o<QB, BQ, SPARSE>(a, ti.head, ti.qt, wave, lane, acc, l);
+  store_o<D, QB, BQ, SPARSE>(a, ti.head, ti.qt, wave, lane, acc, l);
 }
 
-template <int QB, bool SPARSE>
+template <int D, bool SPARSE>
 __global__ void __launch_bounds__(512) attn_static_kernel(AttnArgs a) {
-  __shared__ __attribute__((aligned(16))) uint16_t sKV[2 * kTileElems];
-  attn_kernel_body<QB, SPARSE, kStatic>(a, sKV);
+  __shared__ __attribute__((aligned(16))) uint16_t sKV[2 * Head<D>::TILE];
+  attn_kernel_body<D, SPARSE, kStatic>(a, sKV);
 }
 
-template <int QB, bool SPARSE>
+template <int D, bool SPARSE>
 __global__ void __launch_bounds__(512) attn_online_kernel(AttnArgs a) {
-  __shared__ __attribute__((aligned(16))) uint16_t sKV[2 * kTileElems];
-  attn_kernel_body<QB, SPARSE, kOnline>(a, sKV);
+  __shared__ __attribute__((aligned(16))) uint16_t sKV[2 * Head<D>::TILE];
+  attn_kernel_body<D, SPARSE, kOnline>(a, sKV);
 }
 
 // Block-sparse iteration lists: for each (head, query tile) the ascending KV blocks kept by any of the
@@ -596,27 +641,31 @@ __global__ void __launch_bounds__(256) compact_kernel(CompactArgs a) {
   if (threadIdx.x == 0) a.list_len[tile] = base;
 }
 
-template <bool SPARSE>
+template <int D, bool SPARSE>
 hipError_t launch_attn(const AttnArgs& a, hipStream_t s) {
-  hipLaunchKernelGGL(kv_prep_kernel, dim3(a.nb, a.g.heads), dim3(256), 0, s, a);
+  hipLaunchKernelGGL(kv_prep_kernel<D>, dim3(a.nb, a.g.heads), dim3(256), 0, s, a);
   hipError_t e0 = hipGetLastError();
   if (e0 != hipSuccess) return e0;
   const int blocks = a.per_xcd * 8;
   // Both softmax kernels are queued; each checks the weight bound itself and the one that does
   // not apply returns before touching any data.
-  hipLaunchKernelGGL((attn_static_kernel<kQB, SPARSE>), dim3(blocks), dim3(512), 0, s, a);
+  hipLaunchKernelGGL((attn_static_kernel<D, SPARSE>), dim3(blocks), dim3(64 * kNW), 0, s, a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL((attn_online_kernel<kQB, SPARSE>), dim3(blocks), dim3(512), 0, s, a);
+  hipLaunchKernelGGL((attn_online_kernel<D, SPARSE>), dim3(blocks), dim3(64 * kNW), 0, s, a);
   return hipGetLastError();
 }
 
 }  // namespace
 
-int attn_query_tile() { return kBQ; }
+int attn_query_tile(int head_dim) { return head_dim == 128 ? Head<128>::BQ : Head<96>::BQ; }
 
-hipError_t launch_attn_dense(const AttnArgs& a, hipStream_t s) { return launch_attn<false>(a, s); }
-hipError_t launch_attn_sparse(const AttnArgs& a, hipStream_t s) { return launch_attn<true>(a, s); }
+hipError_t launch_attn_dense(const AttnArgs& a, hipStream_t s) {
+  return a.head_dim == 128 ? launch_attn<128, false>(a, s) : launch_attn<96, false>(a, s);
+}
+hipError_t launch_attn_sparse(const AttnArgs& a, hipStream_t s) {
+  return a.head_dim == 128 ? launch_attn<128, true>(a, s) : launch_attn<96, true>(a, s);
+}
 
 hipError_t launch_compact(const CompactArgs& a, hipStream_t s) {
   hipLaunchKernelGGL(compact_kernel, dim3(a.heads * a.nqt), dim3(256), 0, s, a);

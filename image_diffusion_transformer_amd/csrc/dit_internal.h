@@ -6,11 +6,16 @@
 
 namespace dit {
 
-constexpr int kHeadDim = 96;     // 5376 hidden / 56 heads
+constexpr int kHeadDim = 96;     // 5376 hidden / 56 heads; head dim 128 is the other instantiation
 constexpr int kBlock = 128;      // router block and KV tile: 128 consecutive tokens
-constexpr int kAxisDim = 32;     // RoPE channels per axis (t, h, w)
-constexpr int kPairs = 16;       // RoPE pairs per axis
-constexpr int kRopeRow = 32;     // floats per RoPE table row: 16 cos then 16 sin
+
+// RoPE channels of axis a (0 = t, 1 = h, 2 = w): three chunks of 32 at head dim 96; 44, 42, 42 at 128
+// (the nearest-equal split into even widths).  Pair i of axis a rotates by pos * theta^(-2i/width).
+constexpr int rope_width(int d, int axis) { return d == 96 ? 32 : (axis == 0 ? 44 : 42); }
+// Floats per RoPE table row: cos of the axis's pairs, then (from half the row) their sin.
+constexpr int rope_row_floats(int d) { return d == 96 ? 32 : 44; }
+// Fragments of one (head, 128-key tile) image: 4 d/16 K^ plus 8 d/32 V^T fragments of 1 KB.
+constexpr int tile_frags(int d) { return 4 * (d / 16) + 8 * (d / 32); }
 
 // Exact unsigned division of n < 2^31 by a runtime divisor d >= 1:
 // q = (n * m) >> s with s = 32 + ceil(log2 d), m = ceil(2^s / d) (fits in 33 bits).
@@ -48,7 +53,9 @@ struct AttnArgs {
   int nq, nk;             // query and key token counts (both N for grid calls)
   const int* q_pos;       // null for grid calls; else int32 [nq][3] (t, h, w) explicit positions
   const int* k_pos;       // null for grid calls; else int32 [nk][3]
-  int max_pos;            // explicit positions: rows of the shared RoPE table (coordinates are clamped)
+  int max_pos;            // explicit positions: rows per axis section of the RoPE table (coordinates clamped)
+  int rope_sec[3];        // explicit positions: first table row of each axis's section
+  int head_dim;           // 96 or 128
   float qscale;           // log2(e) / sqrt(96): softmax runs in base 2
   float eps;
   int nqt;                // query tiles per head
@@ -70,9 +77,10 @@ struct RouteArgs {
   float eps;
   int nb;
   int keep;
-  float* pooled;          // [2][heads][nb][96] block means of q (0) and k (1)
+  float* pooled;          // [2][heads][nb][d] block means of q (0) and k (1)
   uint32_t* scores;       // [heads][nb][nb] order keys of the block scores (nb <= route_topk_max_blocks())
   unsigned char* mask;    // [heads][nb][nb]
+  int head_dim;           // 96 or 128
 };
 
 struct CompactArgs {
@@ -104,11 +112,11 @@ struct SwigluArgs {
   int chunks;             // workgroups per token row (set by launch_swiglu)
 };
 
-// Bytes of one (head, 128-key tile) fragment image: 48 fragments of 64 lanes x 16 bytes.
-constexpr size_t kTileImageBytes = 48 * 1024;
+// Bytes of one (head, 128-key tile) fragment image: fragments of 64 lanes x 16 bytes.
+constexpr size_t tile_image_bytes(int d) { return (size_t)tile_frags(d) * 1024; }
 
-// Query tile of the attention kernel (tokens per workgroup) -- a multiple of kBlock.
-int attn_query_tile();
+// Query tile of the attention kernel (tokens per workgroup) at head dim d -- a multiple of kBlock.
+int attn_query_tile(int head_dim);
 
 hipError_t launch_attn_dense(const AttnArgs& a, hipStream_t s);
 hipError_t launch_attn_sparse(const AttnArgs& a, hipStream_t s);

@@ -34,16 +34,20 @@ typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 __device__ __forceinline__ float bf_lo(uint32_t u) { return __uint_as_float(u << 16); }
 __device__ __forceinline__ float bf_hi(uint32_t u) { return __uint_as_float(u & 0xffff0000u); }
 
-// LDS row stride of a staged token row: 96 bf16 = 48 words, padded to 52 so that the 16-byte
-// reads of consecutive rows by consecutive lanes cover all 64 banks without conflict.
-constexpr int kRowWords = 52;
+// LDS row stride of a staged token row: d bf16 = d/2 words, padded by 4 (52 or 68 words) so that
+// the 16-byte reads of consecutive rows by consecutive lanes cover all 64 banks without conflict.
+template <int D>
+constexpr int row_words() { return D / 2 + 4; }
 constexpr int kPoolPart = 64;   // tokens staged at a time (half a block)
 
 // One wave per (block, head, tensor), over the block's two halves in token order: stage the
 // half's rows in LDS (coalesced 16-byte loads), compute each token's reciprocal RMS (sequential
 // channel sum) and RoPE table rows, then let lane p < 48 walk the tokens in ascending order,
 // normalising and rotating its channel pair and adding it to the running block sums.
+template <int D>
 __global__ void __launch_bounds__(64) route_pool_kernel(RouteArgs a) {
+  constexpr int kRowWords = row_words<D>(), CH = D / 8, RS = rope_row_floats(D);
+  constexpr int P0 = rope_width(D, 0) / 2, P1 = rope_width(D, 1) / 2;
   __shared__ __attribute__((aligned(16))) uint32_t xs[kPoolPart * kRowWords];
   __shared__ float rs[kPoolPart];
   __shared__ int rowoff[kPoolPart][3];   // float offsets of the t, h and w rows of the RoPE table
@@ -53,32 +57,33 @@ __global__ void __launch_bounds__(64) route_pool_kernel(RouteArgs a) {
   const int n0 = b * kBlock;
   const int cnt = min(kBlock, a.g.N - n0);
   const float* wv = tensor ? a.wk : a.wq;
-  const int p = min(lane, kHeadDim / 2 - 1);
+  const int p = min(lane, D / 2 - 1);
   const float we = wv[2 * p], wf = wv[2 * p + 1];
-  const int axis = p / kPairs, i = p % kPairs;
+  const int axis = (p >= P0) + (p >= P0 + P1);
+  const int i = p - (axis == 0 ? 0 : (axis == 1 ? P0 : P0 + P1));
   float acc_e = 0.f, acc_f = 0.f;
   for (int m0 = 0; m0 < cnt; m0 += kPoolPart) {
     const int part_cnt = min(kPoolPart, cnt - m0);
     // Rows past the tail block's last token repeat that token; they are staged but never read.
-    constexpr int kChunks = kPoolPart * 12 / 64;   // 16-byte chunks per lane
+    constexpr int kChunks = kPoolPart * CH / 64;   // 16-byte chunks per lane
     u32x4 v[kChunks];
 #pragma unroll
     for (int k = 0; k < kChunks; ++k) {
-      const int c = lane + 64 * k, t = c / 12, part = c - 12 * t;
+      const int c = lane + 64 * k, t = c / CH, part = c - CH * t;
       const int tl = min(t, part_cnt - 1);
-      v[k] = *(const u32x4*)(X + ((size_t)(n0 + m0 + tl) * a.g.heads + head) * kHeadDim + part * 8);
+      v[k] = *(const u32x4*)(X + ((size_t)(n0 + m0 + tl) * a.g.heads + head) * D + part * 8);
     }
     __syncthreads();   // the previous half's rows are no longer read
 #pragma unroll
     for (int k = 0; k < kChunks; ++k) {
-      const int c = lane + 64 * k, t = c / 12, part = c - 12 * t;
+      const int c = lane + 64 * k, t = c / CH, part = c - CH * t;
       *(u32x4*)(xs + t * kRowWords + part * 4) = v[k];
     }
     __syncthreads();
     if (lane < part_cnt) {
       float ss = 0.f;
 #pragma unroll
-      for (int j = 0; j < 12; ++j) {
+      for (int j = 0; j < CH; ++j) {
         const u32x4 x = *(const u32x4*)(xs + lane * kRowWords + 4 * j);
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
@@ -87,13 +92,13 @@ __global__ void __launch_bounds__(64) route_pool_kernel(RouteArgs a) {
           ss = __fadd_rn(ss, __fmul_rn(hi, hi));
         }
       }
-      const float ms = __fdiv_rn(ss, (float)kHeadDim);
+      const float ms = __fdiv_rn(ss, (float)D);
       rs[lane] = __fdiv_rn(1.0f, __builtin_sqrtf(__fadd_rn(ms, a.eps)));
       const int n = n0 + m0 + lane;
       const int t = n / (a.g.H * a.g.W), h = (n / a.g.W) % a.g.H, w = n % a.g.W;
-      rowoff[lane][0] = t * kRopeRow;
-      rowoff[lane][1] = (a.g.T + h) * kRopeRow;
-      rowoff[lane][2] = (a.g.T + a.g.H + w) * kRopeRow;
+      rowoff[lane][0] = t * RS;
+      rowoff[lane][1] = (a.g.T + h) * RS;
+      rowoff[lane][2] = (a.g.T + a.g.H + w) * RS;
     }
     __syncthreads();
 #pragma unroll 8
@@ -102,7 +107,7 @@ __global__ void __launch_bounds__(64) route_pool_kernel(RouteArgs a) {
       const float r = rs[n];
       const int ro = rowoff[n][axis];
       const float c = a.rope[ro + i];
-      const float s = a.rope[ro + kPairs + i];
+      const float s = a.rope[ro + RS / 2 + i];
       const float xe = __fmul_rn(__fmul_rn(bf_lo(x2), r), we);
       const float xf = __fmul_rn(__fmul_rn(bf_hi(x2), r), wf);
       const float ye = __fsub_rn(__fmul_rn(xe, c), __fmul_rn(xf, s));
@@ -111,9 +116,9 @@ __global__ void __launch_bounds__(64) route_pool_kernel(RouteArgs a) {
       acc_f = __fadd_rn(acc_f, yf);
     }
   }
-  if (lane >= kHeadDim / 2) return;
+  if (lane >= D / 2) return;
   const float fc = (float)cnt;
-  float* out = a.pooled + (((size_t)tensor * a.g.heads + head) * a.nb + b) * kHeadDim;
+  float* out = a.pooled + (((size_t)tensor * a.g.heads + head) * a.nb + b) * D;
   out[2 * p] = __fdiv_rn(acc_e, fc);
   out[2 * p + 1] = __fdiv_rn(acc_f, fc);
 }
@@ -141,17 +146,18 @@ __device__ __forceinline__ int block_sum256(int v, int* red) {
 constexpr int kScoreTile = 64;
 constexpr int kTileStride = kScoreTile + 1;
 
+template <int D>
 __global__ void __launch_bounds__(256) route_score_kernel(RouteArgs a) {
-  __shared__ float qs[kHeadDim * kTileStride];
-  __shared__ float ks[kHeadDim * kTileStride];
+  __shared__ float qs[D * kTileStride];
+  __shared__ float ks[D * kTileStride];
   const int nb = a.nb;
   const int j0 = blockIdx.x * kScoreTile, i0 = blockIdx.y * kScoreTile, head = blockIdx.z;
   const int tid = threadIdx.x;
-  const f32x4* qbar = (const f32x4*)(a.pooled + ((size_t)head * nb + i0) * kHeadDim);
-  const f32x4* kbar = (const f32x4*)(a.pooled + ((size_t)(a.g.heads + head) * nb + j0) * kHeadDim);
-  constexpr int kVec = kScoreTile * kHeadDim / 4;
+  const f32x4* qbar = (const f32x4*)(a.pooled + ((size_t)head * nb + i0) * D);
+  const f32x4* kbar = (const f32x4*)(a.pooled + ((size_t)(a.g.heads + head) * nb + j0) * D);
+  constexpr int kVec = kScoreTile * D / 4;
   for (int f = tid; f < kVec; f += 256) {
-    const int row = f / (kHeadDim / 4), c4 = f - row * (kHeadDim / 4);
+    const int row = f / (D / 4), c4 = f - row * (D / 4);
     const f32x4 zero = {0.f, 0.f, 0.f, 0.f};
     const f32x4 qv = i0 + row < nb ? qbar[f] : zero;
     const f32x4 kv = j0 + row < nb ? kbar[f] : zero;
@@ -169,7 +175,7 @@ __global__ void __launch_bounds__(256) route_score_kernel(RouteArgs a) {
 #pragma unroll
     for (int z = 0; z < 4; ++z) acc[u][z] = 0.f;
 #pragma unroll 4
-  for (int c = 0; c < kHeadDim; ++c) {
+  for (int c = 0; c < D; ++c) {
     float qv[4], kv[4];
 #pragma unroll
     for (int u = 0; u < 4; ++u) qv[u] = qs[c * kTileStride + ty + 16 * u];
@@ -238,22 +244,23 @@ __global__ void __launch_bounds__(256) route_topk_kernel(RouteArgs a) {
 }
 
 // Large-nb path (nb > route_topk_max_blocks()): one workgroup per score row, scores and order keys in LDS.
+template <int D>
 __global__ void __launch_bounds__(256) route_select_kernel(RouteArgs a) {
   extern __shared__ uint32_t keys[];   // [nb] scores, then order keys
-  __shared__ float qrow[kHeadDim];
+  __shared__ float qrow[D];
   __shared__ int red[4];
   __shared__ int scan[256];
   const int nb = a.nb;
   const int row = blockIdx.x;          // head * nb + i
   const int head = row / nb, i = row - head * nb;
-  const float* qbar = a.pooled + ((size_t)head * nb + i) * kHeadDim;
-  const float* kbar = a.pooled + ((size_t)(a.g.heads + head) * nb) * kHeadDim;
-  if (threadIdx.x < kHeadDim) qrow[threadIdx.x] = qbar[threadIdx.x];
+  const float* qbar = a.pooled + ((size_t)head * nb + i) * D;
+  const float* kbar = a.pooled + ((size_t)(a.g.heads + head) * nb) * D;
+  if (threadIdx.x < D) qrow[threadIdx.x] = qbar[threadIdx.x];
   __syncthreads();
   for (int j = threadIdx.x; j < nb; j += 256) {
-    const f32x4* kv = (const f32x4*)(kbar + (size_t)j * kHeadDim);
+    const f32x4* kv = (const f32x4*)(kbar + (size_t)j * D);
     float acc = 0.f;
-    for (int c4 = 0; c4 < kHeadDim / 4; ++c4) {
+    for (int c4 = 0; c4 < D / 4; ++c4) {
       const f32x4 k4 = kv[c4];
 #pragma unroll
       for (int e = 0; e < 4; ++e) acc = __fadd_rn(acc, __fmul_rn(qrow[4 * c4 + e], k4[e]));
@@ -303,15 +310,15 @@ __global__ void __launch_bounds__(256) route_select_kernel(RouteArgs a) {
   }
 }
 
-}  // namespace
 
-hipError_t launch_route(const RouteArgs& a, hipStream_t s) {
-  hipLaunchKernelGGL(route_pool_kernel, dim3(a.nb, a.g.heads, 2), dim3(64), 0, s, a);
+template <int D>
+hipError_t launch_route_d(const RouteArgs& a, hipStream_t s) {
+  hipLaunchKernelGGL(route_pool_kernel<D>, dim3(a.nb, a.g.heads, 2), dim3(64), 0, s, a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   if (a.nb <= route_topk_max_blocks()) {
     const unsigned tiles = (unsigned)((a.nb + kScoreTile - 1) / kScoreTile);
-    hipLaunchKernelGGL(route_score_kernel, dim3(tiles, tiles, a.g.heads), dim3(256), 0, s, a);
+    hipLaunchKernelGGL(route_score_kernel<D>, dim3(tiles, tiles, a.g.heads), dim3(256), 0, s, a);
     e = hipGetLastError();
     if (e != hipSuccess) return e;
     const unsigned rows = (unsigned)(((long long)a.g.heads * a.nb + 3) / 4);
@@ -325,11 +332,18 @@ hipError_t launch_route(const RouteArgs& a, hipStream_t s) {
   }
   const size_t lds = (size_t)a.nb * sizeof(uint32_t);
   if (lds > 64 * 1024) {
-    e = hipFuncSetAttribute((const void*)route_select_kernel, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+    e = hipFuncSetAttribute((const void*)route_select_kernel<D>, hipFuncAttributeMaxDynamicSharedMemorySize,
+                            (int)lds);
     if (e != hipSuccess) return e;
   }
-  hipLaunchKernelGGL(route_select_kernel, dim3(a.g.heads * a.nb), dim3(256), lds, s, a);
+  hipLaunchKernelGGL(route_select_kernel<D>, dim3(a.g.heads * a.nb), dim3(256), lds, s, a);
   return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_route(const RouteArgs& a, hipStream_t s) {
+  return a.head_dim == 128 ? launch_route_d<128>(a, s) : launch_route_d<96>(a, s);
 }
 
 }  // namespace dit

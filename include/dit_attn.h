@@ -21,12 +21,14 @@
  *  - q, k, v, o: bfloat16, shape [N][heads][head_dim], contiguous, device memory.
  *  - wq, wk: float32 [head_dim] RMSNorm weights, shared by all heads, device memory.
  *  - RMSNorm: x * w / sqrt(mean_c(x_c^2) + eps) over the head_dim channels of
- *    one (token, head).  RoPE: channels [0,32) rotate with t, [32,64) with h,
- *    [64,96) with w; pairs (2i, 2i+1); angle pos * rope_theta^(-2i/32); the
+ *    one (token, head).  RoPE: at head_dim 96 channels [0,32) rotate with t,
+ *    [32,64) with h, [64,96) with w; at head_dim 128 (the SubBlock precondition in
+ *    the report's limits section; the pages give no split, the nearest-equal even
+ *    one is used) [0,44) with t, [44,86) with h, [86,128) with w.  Within a chunk
+ *    of width c the pairs are (2i, 2i+1) at angle pos * rope_theta^(-2i/c); the
  *    pair (a, b) becomes (a cos - b sin, a sin + b cos).  V is untouched.
  *  - Attention: O = softmax(Q^ K^T / sqrt(head_dim)) V, every query sees every key.
- *  - Only head_dim == 96 and block == 128 are implemented (DIT_ERR_UNSUPPORTED
- *    otherwise).
+ *  - head_dim must be 96 or 128 and block 128 (DIT_ERR_UNSUPPORTED otherwise).
  *  - All pointers are owned by the caller.  The library allocates no device
  *    memory; scratch space comes from `workspace` (see dit_attn_workspace_bytes).
  *  - Every call is asynchronous on `hip_stream` (a hipStream_t; NULL means the
@@ -49,7 +51,7 @@ extern "C" {
 typedef enum {
   DIT_OK = 0,
   DIT_ERR_INVALID_ARG = 1, /* null pointer, bad size, non-finite theta/eps, sparsity outside [0,1) */
-  DIT_ERR_UNSUPPORTED = 2, /* head_dim != 96, block != 128, grid too large for one call       */
+  DIT_ERR_UNSUPPORTED = 2, /* head_dim not 96/128, block != 128, grid too large for one call  */
   DIT_ERR_WORKSPACE = 3,   /* workspace missing or smaller than dit_attn_workspace_bytes()    */
   DIT_ERR_HIP = 4          /* a HIP runtime call failed; the HIP error string is in last_error */
 } dit_status;

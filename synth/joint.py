@@ -33,6 +33,7 @@ class JointWorkload:
     queries: str = "target"      # "target" or "all"
     theta: float = 10000.0
     eps: float = 1e-6
+    head_dim: int = HEAD_DIM     # 96 (the model's) or 128
     notes: str = field(default="", compare=False)
 
     @property
@@ -61,6 +62,8 @@ JOINT_WORKLOADS = {
                       notes="Nkv = 50 + 256 + 240 + 768 = 1314, queries = 768 target tokens"),
         JointWorkload("j_all", 33, ((8, 8),), (2, 12, 10), 2, seed=22, queries="all",
                       notes="Nkv = Nq = 33 + 64 + 240 = 337"),
+        JointWorkload("j_small128", 50, ((16, 16), (12, 20)), (3, 16, 16), 3, seed=24, head_dim=128,
+                      notes="j_small's sequence at head dim 128"),
         JointWorkload("j_edit2", 512, ((256, 256), (256, 256)), (1, 256, 256), 56, seed=23,
                       notes="image edit with 2 reference images: 197,120 keys, 65,536 target queries"),
     ]
@@ -104,12 +107,13 @@ def make_joint_inputs(wl: JointWorkload | str) -> JointInputs:
         wl = JOINT_WORKLOADS[wl]
     k_pos = sequence_positions(wl)
     q_pos = k_pos[wl.Nkv - wl.Nq:] if wl.queries == "target" else k_pos
-    q = f32_to_bf16_bits(_draw(wl.seed, 0, (wl.Nq, wl.heads, HEAD_DIM)))
-    k = f32_to_bf16_bits(_draw(wl.seed, 1, (wl.Nkv, wl.heads, HEAD_DIM)))
-    v = f32_to_bf16_bits(_draw(wl.seed, 2, (wl.Nkv, wl.heads, HEAD_DIM)))
+    d = wl.head_dim
+    q = f32_to_bf16_bits(_draw(wl.seed, 0, (wl.Nq, wl.heads, d)))
+    k = f32_to_bf16_bits(_draw(wl.seed, 1, (wl.Nkv, wl.heads, d)))
+    v = f32_to_bf16_bits(_draw(wl.seed, 2, (wl.Nkv, wl.heads, d)))
     g = np.random.Generator(np.random.PCG64(np.random.SeedSequence([wl.seed, 7])))
-    wq = (1.0 + 0.1 * g.standard_normal(HEAD_DIM)).astype(np.float32)
-    wk = (1.0 + 0.1 * g.standard_normal(HEAD_DIM)).astype(np.float32)
+    wq = (1.0 + 0.1 * g.standard_normal(d)).astype(np.float32)
+    wk = (1.0 + 0.1 * g.standard_normal(d)).astype(np.float32)
     max_pos = int(k_pos.max()) + 1
     return JointInputs(wl, BF16Tensor(q), BF16Tensor(k), BF16Tensor(v), np.ascontiguousarray(q_pos),
                        np.ascontiguousarray(k_pos), max_pos, wq, wk)

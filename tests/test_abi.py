@@ -56,7 +56,9 @@ def test_workspace_bytes(lib):
     assert big < 4100 * 48 * 1024 + 2 * 4100 * 96 * 4 + 4100 * 4100 * 4
     assert n >= 56 * -(-N // 512) * nb * 4                  # sparse: KV lists per 512-token query tile
     assert n >= 56 * nb * 48 * 1024 + 56 * -(-N // 512) * nb * 4   # K^/V fragment images + sparse lists
-    assert dit.dit_attn_workspace_bytes(31, 48, 84, 56, 128) == 0   # head_dim 128 unsupported
+    assert dit.dit_attn_workspace_bytes(31, 48, 84, 56, 64) == 0    # head_dim 64 unsupported
+    n128 = dit.dit_attn_workspace_bytes(31, 48, 84, 42, 128)        # 42 heads x 128: 64 KB tile images
+    assert n128 >= 42 * nb * 64 * 1024 + 2 * 42 * nb * 128 * 4 + 42 * nb * nb * 4
     assert dit.dit_attn_workspace_bytes(31, 48, 84, 56, 96, 64) == 0
     assert dit.dit_attn_workspace_bytes(0, 48, 84, 56) == 0
 
@@ -97,7 +99,7 @@ def _sparse(lib, **kw):
     (dict(q=FAKE + 2), B.DIT_ERR_INVALID_ARG, "aligned"),
     (dict(T=0), B.DIT_ERR_INVALID_ARG, "grid"),
     (dict(heads=-1), B.DIT_ERR_INVALID_ARG, "grid"),
-    (dict(d=128), B.DIT_ERR_UNSUPPORTED, "head_dim"),
+    (dict(d=64), B.DIT_ERR_UNSUPPORTED, "head_dim"),
     (dict(T=4000, H=4000, W=4), B.DIT_ERR_UNSUPPORTED, "exceeds"),
     (dict(theta=0.0), B.DIT_ERR_INVALID_ARG, "rope_theta"),
     (dict(theta=float("inf")), B.DIT_ERR_INVALID_ARG, "rope_theta"),
@@ -170,7 +172,7 @@ def _joint(lib, **kw):
     (dict(nk=-3), B.DIT_ERR_INVALID_ARG, "token counts"),
     (dict(maxp=0), B.DIT_ERR_INVALID_ARG, "max_pos"),
     (dict(maxp=(1 << 20) + 1), B.DIT_ERR_UNSUPPORTED, "max_pos"),
-    (dict(d=128), B.DIT_ERR_UNSUPPORTED, "head_dim"),
+    (dict(d=64), B.DIT_ERR_UNSUPPORTED, "head_dim"),
     (dict(nk=30_000_000), B.DIT_ERR_UNSUPPORTED, "exceeds"),
     (dict(theta=-1.0), B.DIT_ERR_INVALID_ARG, "rope_theta"),
     (dict(ws=None), B.DIT_ERR_WORKSPACE, "workspace"),

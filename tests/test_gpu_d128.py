@@ -1,0 +1,156 @@
+"""GPU parity at head dim 128 (RoPE chunks 44/42/42): dense, router, block-sparse and joint attention
+through the C ABI against the fp64 oracle.  Same tolerances as head dim 96: O within max-abs 2e-2 and
+relative L2 1e-2, router masks bit-exact, equal-by-construction cases bitwise equal."""
+import numpy as np
+import pytest
+import torch
+
+import image_diffusion_transformer_amd as dit
+from oracle import attention as A
+from oracle import router as R
+from synth import WORKLOADS, custom_workload, make_inputs, make_joint_inputs
+
+pytestmark = pytest.mark.gpu
+DEV = torch.device("cuda:0")
+MAX_ABS, REL_L2 = 2e-2, 1e-2
+
+
+def upload(x):
+    def t(b):
+        return torch.from_numpy(b.bits.view(np.int16)).to(DEV).view(torch.bfloat16)
+    return (t(x.q), t(x.k), t(x.v), torch.from_numpy(x.wq).to(DEV), torch.from_numpy(x.wk).to(DEV))
+
+
+def check_close(got, ref, what):
+    got = got.astype(np.float64)
+    err = np.abs(got - ref)
+    maxabs = float(err.max())
+    rel = float(np.linalg.norm(err) / max(np.linalg.norm(ref), 1e-30))
+    print(f"{what}: max_abs={maxabs:.3e} rel_l2={rel:.3e}", flush=True)
+    assert np.all(np.isfinite(got)), what
+    assert maxabs <= MAX_ABS and rel <= REL_L2, (what, maxabs, rel)
+
+
+@pytest.mark.parametrize("name", ["t128", "s1_128", "s3_128", "s4_128"])
+def test_dense_d128_all_rows(name):
+    x = make_inputs(name)
+    wl = x.workload
+    print(f"case dense d128 {name}", flush=True)
+    q, k, v, wq, wk = upload(x)
+    o = dit.dit_attn_dense(q, k, v, wq, wk, (wl.T, wl.H, wl.W), wl.theta, wl.eps)
+    torch.cuda.synchronize()
+    assert o.shape == (wl.N, wl.heads, 128)
+    ref = A.attention(x.q, x.k, x.v, x.wq, x.wk, wl.T, wl.H, wl.W, wl.theta, wl.eps)
+    check_close(o.float().cpu().numpy(), ref, f"dense {name}")
+
+
+def test_dense_d128_online_mode():
+    x = make_inputs("s3_128")
+    wl = x.workload
+    q, k, v, wq, wk = upload(x)
+    wq2 = wq.clone()
+    wq2[7] = 4.0                      # logit bound > 48: the running-max kernel runs
+    o = dit.dit_attn_dense(q, k, v, wq2, wk, (wl.T, wl.H, wl.W), wl.theta, wl.eps)
+    torch.cuda.synchronize()
+    wqn = x.wq.copy()
+    wqn[7] = 4.0
+    ref = A.attention(x.q, x.k, x.v, wqn, x.wk, wl.T, wl.H, wl.W, wl.theta, wl.eps)
+    check_close(o.float().cpu().numpy(), ref, "dense d128 online")
+
+
+@pytest.mark.parametrize("name", ["s1_128", "s3_128", "s4_128"])
+@pytest.mark.parametrize("sparsity", [0.5, 0.75])
+def test_route_d128_bit_exact(name, sparsity):
+    x = make_inputs(name)
+    wl = x.workload
+    q, k, v, wq, wk = upload(x)
+    m = dit.dit_attn_route(q, k, wq, wk, (wl.T, wl.H, wl.W), sparsity, wl.theta, wl.eps)
+    torch.cuda.synchronize()
+    ref = R.route_mask(x.q, x.k, x.wq, x.wk, wl.T, wl.H, wl.W, sparsity, wl.theta, wl.eps)
+    got = m.cpu().numpy()
+    bad = np.argwhere(np.any(got != ref, axis=2))
+    assert bad.size == 0, f"mismatched (head, row) pairs: {bad[:10].tolist()}"
+
+
+@pytest.mark.parametrize("name", ["s3_128", "s4_128"])
+def test_block_sparse_d128_on_oracle_mask(name):
+    x = make_inputs(name)
+    wl = x.workload
+    q, k, v, wq, wk = upload(x)
+    mask = R.route_mask(x.q, x.k, x.wq, x.wk, wl.T, wl.H, wl.W, 0.75, wl.theta, wl.eps)
+    o = dit.dit_attn_block_sparse(q, k, v, wq, wk, (wl.T, wl.H, wl.W), torch.from_numpy(mask).to(DEV),
+                                  wl.theta, wl.eps)
+    torch.cuda.synchronize()
+    ref = A.attention(x.q, x.k, x.v, x.wq, x.wk, wl.T, wl.H, wl.W, wl.theta, wl.eps, mask=mask)
+    check_close(o.float().cpu().numpy(), ref, f"sparse d128 {name}")
+
+
+def test_block_sparse_d128_all_ones_equals_dense_bitwise_and_empty_rows():
+    x = make_inputs("s4_128")
+    wl = x.workload
+    q, k, v, wq, wk = upload(x)
+    g = (wl.T, wl.H, wl.W)
+    dense = dit.dit_attn_dense(q, k, v, wq, wk, g, wl.theta, wl.eps)
+    ones = torch.ones((wl.heads, wl.nb, wl.nb), dtype=torch.uint8, device=DEV)
+    sp = dit.dit_attn_block_sparse(q, k, v, wq, wk, g, ones, wl.theta, wl.eps)
+    rng = np.random.default_rng(5)
+    mask = (rng.random((wl.heads, wl.nb, wl.nb)) < 0.3).astype(np.uint8)
+    mask[0, 3, :] = 0
+    sr = dit.dit_attn_block_sparse(q, k, v, wq, wk, g, torch.from_numpy(mask).to(DEV), wl.theta, wl.eps)
+    torch.cuda.synchronize()
+    assert torch.equal(dense, sp)
+    got = sr.float().cpu().numpy()
+    assert np.all(got[3 * 128:4 * 128, 0] == 0)
+    ref = A.attention(x.q, x.k, x.v, x.wq, x.wk, wl.T, wl.H, wl.W, wl.theta, wl.eps, mask=mask)
+    check_close(got, ref, "sparse d128 random mask")
+
+
+def test_joint_d128_all_rows_and_grid_positions_bitwise():
+    x = make_joint_inputs("j_small128")
+    wl = x.workload
+
+    def t(b):
+        return torch.from_numpy(b.bits.view(np.int16)).to(DEV).view(torch.bfloat16)
+    q, k, v = t(x.q), t(x.k), t(x.v)
+    wq, wk = torch.from_numpy(x.wq).to(DEV), torch.from_numpy(x.wk).to(DEV)
+    o = dit.dit_attn_joint(q, k, v, wq, wk, torch.from_numpy(x.q_pos).to(DEV), torch.from_numpy(x.k_pos).to(DEV),
+                           x.max_pos, wl.theta, wl.eps)
+    # the grid call and the joint call with the grid's positions agree bit for bit
+    gx = make_inputs("s3_128")
+    gw = gx.workload
+    gq, gk, gv, gwq, gwk = upload(gx)
+    t_, h_, w_ = A.positions(gw.T, gw.H, gw.W)
+    pos = torch.from_numpy(np.stack([t_, h_, w_], axis=1).astype(np.int32)).to(DEV)
+    og = dit.dit_attn_joint(gq, gk, gv, gwq, gwk, pos, pos, max(gw.T, gw.H, gw.W), gw.theta, gw.eps)
+    od = dit.dit_attn_dense(gq, gk, gv, gwq, gwk, (gw.T, gw.H, gw.W), gw.theta, gw.eps)
+    torch.cuda.synchronize()
+    ref = A.attention_joint(x.q, x.k, x.v, x.wq, x.wk, x.q_pos, x.k_pos, wl.theta, wl.eps)
+    check_close(o.float().cpu().numpy(), ref, "joint d128 j_small128")
+    assert torch.equal(og, od)
+
+
+def test_full_size_d128_dense_and_sparse_sampled():
+    wl = WORKLOADS["v5s128"]
+    x = make_inputs(wl)
+    print("case full v5 d128", flush=True)
+    q, k, v, wq, wk = upload(x)
+    g = (wl.T, wl.H, wl.W)
+    ws = dit.workspace_for(q, g)
+    od = dit.dit_attn_dense(q, k, v, wq, wk, g, wl.theta, wl.eps, workspace=ws)
+    mask = dit.dit_attn_route(q, k, wq, wk, g, wl.sparsity, wl.theta, wl.eps, workspace=ws)
+    osp = dit.dit_attn_block_sparse(q, k, v, wq, wk, g, mask, wl.theta, wl.eps, workspace=ws)
+    torch.cuda.synchronize()
+    heads = [0, 41]
+    rows = np.concatenate([np.arange(0, 128), np.arange(wl.N - 64, wl.N)])
+    idx = torch.from_numpy(rows).to(DEV)
+    m_gpu = mask.cpu().numpy()
+    m_ref = R.route_mask(x.q, x.k, x.wq, x.wk, wl.T, wl.H, wl.W, wl.sparsity, wl.theta, wl.eps, heads=heads)
+    for i, hd in enumerate(heads):
+        assert np.array_equal(m_gpu[hd], m_ref[i]), f"head {hd} mask differs"
+    ref_d = A.attention(x.q, x.k, x.v, x.wq, x.wk, wl.T, wl.H, wl.W, wl.theta, wl.eps, heads=heads, rows=rows)
+    check_close(od[idx][:, heads].float().cpu().numpy(), ref_d, "dense v5 d128 sampled")
+    full = np.zeros_like(m_gpu)
+    full[heads] = m_ref
+    ref_s = A.attention(x.q, x.k, x.v, x.wq, x.wk, wl.T, wl.H, wl.W, wl.theta, wl.eps, heads=heads, rows=rows,
+                        mask=full)
+    check_close(osp[idx][:, heads].float().cpu().numpy(), ref_s, "sparse v5 d128 sampled")
