@@ -69,7 +69,14 @@ constexpr float kTau = 8.0f;  // lazy-rescale threshold, base-2 log units
 //                             the one in which the S^T accumulator holds the probabilities.
 // Keys past the grid have zero K^ and V.  Head dim 96: 24 + 24 fragments (48 KB); 128: 32 + 32 (64 KB).
 constexpr int kFrag = 512;
-constexpr int kNW = 8;   // waves per attention workgroup (2 per SIMD)
+
+// Shape of the head-dim-128 workgroup: waves and 32-query blocks per wave.
+#ifndef DIT_D128_NW
+#define DIT_D128_NW 8
+#endif
+#ifndef DIT_D128_QB
+#define DIT_D128_QB 1
+#endif
 
 template <int D>
 struct Head {
@@ -79,8 +86,9 @@ struct Head {
   static constexpr int VFRAG0 = 4 * KS;
   static constexpr int FRAGS = 4 * KS + 8 * DB;
   static constexpr int TILE = FRAGS * kFrag;         // bf16 elements of one tile image
-  static constexpr int QB = D == 96 ? 2 : 1;          // 32-query blocks per wave
-  static constexpr int BQ = kNW * QB * 32;            // queries per workgroup
+  static constexpr int NW = D == 96 ? 8 : DIT_D128_NW;   // waves per workgroup
+  static constexpr int QB = D == 96 ? 2 : DIT_D128_QB;   // 32-query blocks per wave
+  static constexpr int BQ = NW * QB * 32;                // queries per workgroup
   static constexpr int RS = rope_row_floats(D);       // floats per RoPE table row
   static constexpr int PAIRS0 = rope_width(D, 0) / 2, PAIRS1 = rope_width(D, 1) / 2;
 };
@@ -203,10 +211,13 @@ __device__ __forceinline__ bool static_bound_holds(const AttnArgs& a, int lane) 
 // blocks QB*w .. QB*w+QB-1.  Block-sparse (QB = 2): wave w holds part w%4 of router blocks 2(w/4) and
 // 2(w/4)+1, so each router block's 128 queries are spread over all four SIMDs (waves w and w+4 share
 // SIMD w%4) and a KV tile kept by few router blocks still keeps every SIMD busy.
-template <int QB, bool SPARSE>
+template <int QB, bool SPARSE, int NW = 8>
 __device__ __forceinline__ int query_block(int wave, int qb) {
-  if constexpr (SPARSE && QB == 2) {
+  if constexpr (SPARSE && QB == 2 && NW == 8) {
     return 8 * (wave >> 2) + 4 * qb + (wave & 3);
+  } else if constexpr (SPARSE && QB == 2) {
+    // four waves: block qb of wave w is part w of router block qb
+    return 4 * qb + wave;
   } else {
     // (block-sparse with one block per wave: waves 0-3 and 4-7 hold the two router blocks of the
     // 256-query tile, each spread over the four SIMDs already)
@@ -214,9 +225,9 @@ __device__ __forceinline__ int query_block(int wave, int qb) {
   }
 }
 // Router block (within the tile) of the wave's query block qb.
-template <int QB, bool SPARSE>
+template <int QB, bool SPARSE, int NW = 8>
 __device__ __forceinline__ int router_block(int wave, int qb) {
-  return query_block<QB, SPARSE>(wave, qb) >> 2;
+  return query_block<QB, SPARSE, NW>(wave, qb) >> 2;
 }
 
 // Q fragments of the wave: load, RMSNorm, RoPE, scale by log2(e)/sqrt(d), pack to bf16 (once per query).
@@ -227,7 +238,7 @@ __device__ __forceinline__ void load_q(const AttnArgs& a, int head, int qt, int 
   const int half = lane >> 5, l32 = lane & 31;
 #pragma unroll
   for (int qb = 0; qb < QB; ++qb) {
-    const int n = qt * BQ + query_block<QB, SPARSE>(wave, qb) * 32 + l32;
+    const int n = qt * BQ + query_block<QB, SPARSE, Head<D>::NW>(wave, qb) * 32 + l32;
     const bool live = n < a.nq;
     u32x4 raw[KS];
     const size_t base = ((size_t)(live ? n : 0) * a.g.heads + head) * D;
@@ -368,7 +379,7 @@ __device__ __forceinline__ void store_o(const AttnArgs& a, int head, int qt, int
   const int half = lane >> 5, l32 = lane & 31;
 #pragma unroll
   for (int qb = 0; qb < QB; ++qb) {
-    const int n = qt * BQ + query_block<QB, SPARSE>(wave, qb) * 32 + l32;
+    const int n = qt * BQ + query_block<QB, SPARSE, Head<D>::NW>(wave, qb) * 32 + l32;
     const float lt = pair_sum(l[qb]);
     const float inv = lt > 0.f ? 1.0f / lt : 0.f;
     if (n < a.nq) {
@@ -486,8 +497,8 @@ __global__ void __launch_bounds__(256) kv_prep_kernel(AttnArgs a) {
 template <int D>
 __device__ __forceinline__ void dma_tile(const uint16_t* src, int wave, int lane, uint16_t* dst) {
   typedef __attribute__((address_space(3))) void lds_void;
-  constexpr int FPW = Head<D>::FRAGS / kNW;
-  static_assert(FPW * kNW == Head<D>::FRAGS, "fragments per wave");
+  constexpr int FPW = Head<D>::FRAGS / Head<D>::NW;
+  static_assert(FPW * Head<D>::NW == Head<D>::FRAGS, "fragments per wave");
 #pragma unroll
   for (int c = 0; c < FPW; ++c) {
     const int f = FPW * wave + c;
@@ -546,7 +557,7 @@ __device__ __forceinline__ void attn_kernel_body(const AttnArgs& a, uint16_t* sK
   const int N = a.nk, nt = ti.ntiles;
   int rbit[QB];
 #pragma unroll
-  for (int qb = 0; qb < QB; ++qb) rbit[qb] = router_block<QB, SPARSE>(wave, qb);
+  for (int qb = 0; qb < QB; ++qb) rbit[qb] = router_block<QB, SPARSE, Head<D>::NW>(wave, qb);
   const uint16_t* img = a.kvf + (size_t)ti.head * a.nb * TILE;
   if (nt > 0) dma_tile<D>(img + (size_t)ti.tile(0, SPARSE) * TILE, wave, lane, sKV);
   bf16x8 qf[QB][KS];
@@ -600,13 +611,13 @@ __device__ __forceinline__ void attn_kernel_body(const AttnArgs& a, uint16_t* sK
 }
 
 template <int D, bool SPARSE>
-__global__ void __launch_bounds__(512) attn_static_kernel(AttnArgs a) {
+__global__ void __launch_bounds__(64 * Head<D>::NW) attn_static_kernel(AttnArgs a) {
   __shared__ __attribute__((aligned(16))) uint16_t sKV[2 * Head<D>::TILE];
   attn_kernel_body<D, SPARSE, kStatic>(a, sKV);
 }
 
 template <int D, bool SPARSE>
-__global__ void __launch_bounds__(512) attn_online_kernel(AttnArgs a) {
+__global__ void __launch_bounds__(64 * Head<D>::NW) attn_online_kernel(AttnArgs a) {
   __shared__ __attribute__((aligned(16))) uint16_t sKV[2 * Head<D>::TILE];
   attn_kernel_body<D, SPARSE, kOnline>(a, sKV);
 }
@@ -649,10 +660,10 @@ hipError_t launch_attn(const AttnArgs& a, hipStream_t s) {
   const int blocks = a.per_xcd * 8;
   // Both softmax kernels are queued; each checks the weight bound itself and the one that does
   // not apply returns before touching any data.
-  hipLaunchKernelGGL((attn_static_kernel<D, SPARSE>), dim3(blocks), dim3(64 * kNW), 0, s, a);
+  hipLaunchKernelGGL((attn_static_kernel<D, SPARSE>), dim3(blocks), dim3(64 * Head<D>::NW), 0, s, a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL((attn_online_kernel<D, SPARSE>), dim3(blocks), dim3(64 * kNW), 0, s, a);
+  hipLaunchKernelGGL((attn_online_kernel<D, SPARSE>), dim3(blocks), dim3(64 * Head<D>::NW), 0, s, a);
   return hipGetLastError();
 }
 
