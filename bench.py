@@ -39,6 +39,8 @@ DESCR = {
     "v5d128": ("dense attention at head dim 128, 124,992 tokens, 42 heads x 128 (the same 5376 hidden width; "
                "RoPE chunks 44/42/42)"),
     "v5s128": ("route + block-sparse attention (sparsity 0.75) at head dim 128, 124,992 tokens, 42 heads x 128"),
+    "s4": "dense attention, small grid 5x24x40 = 4,800 tokens, 2 heads x 96 (contract checks)",
+    "b_mid": "operators around attention on 1,000 tokens, hidden 5376, FFN 14336 (contract checks)",
     "b_v5": ("operators around attention at 124,992 tokens, hidden 5376, FFN 14336: AdaLN update, gated "
              "residual + AdaLN update, SwiGLU, gated residual"),
 }
@@ -195,7 +197,8 @@ def bench_block(args, torch, dit):
         "per_op_ms": {n: round(v, 4) for n, v in per.items()},
         "per_op_gbs": {n: round(b / (per[n] * 1e-3) / 1e9, 1) for n, _, b in ops},
         "roofline": {"bound": "hbm", "achieved": round(dom_gbs, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
-                     "frac": round(dom_gbs / PEAK_HBM_GBS, 4), "traffic": traffic, "kernel": "swiglu_kernel<7>",
+                     "frac": round(dom_gbs / PEAK_HBM_GBS, 4), "traffic": traffic,
+                     "kernel": f"swiglu_kernel<{min(8, -(-wl.ffn // 8 // 256))}>",
                      "kernel_ms": round(per[dom], 4), "bytes_per_launch": dom_bytes},
     }
     if not args.no_cpu_baseline:

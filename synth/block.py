@@ -52,6 +52,7 @@ BLOCK_WORKLOADS = {
         BlockWorkload("b_wide", 29, 8184, 16400, seed=45,
                       notes="hidden 8184 (16 vectors per lane, last one ragged) and FFN 16400 (two "
                             "workgroups per row)"),
+        BlockWorkload("b_min", 1, 8, 8, seed=46, notes="one token, hidden 8, FFN 8: one vector per row"),
         BlockWorkload("b_v5", 124992, 5376, 14336, seed=44,
                       notes="124,992 tokens (5 s 1344x768 clip) at hidden 5376, FFN 14336"),
     ]

@@ -36,7 +36,7 @@ def check(got, ref, what):
     assert worst <= 1.0, (what, worst)
 
 
-@pytest.mark.parametrize("name", ["b_tiny", "b_small", "b_mid", "b_odd", "b_wide"])
+@pytest.mark.parametrize("name", ["b_min", "b_tiny", "b_small", "b_mid", "b_odd", "b_wide"])
 def test_block_ops_all_rows(name):
     x = make_block_inputs(name)
     wl = x.workload

@@ -8,7 +8,7 @@ import torch
 import image_diffusion_transformer_amd as dit
 from oracle import attention as A
 from oracle import router as R
-from synth import WORKLOADS, custom_workload, make_inputs, make_joint_inputs
+from synth import WORKLOADS, bf16_bits_to_f32, f32_to_bf16_bits, make_inputs, make_joint_inputs
 
 pytestmark = pytest.mark.gpu
 DEV = torch.device("cuda:0")
@@ -154,3 +154,21 @@ def test_full_size_d128_dense_and_sparse_sampled():
     ref_s = A.attention(x.q, x.k, x.v, x.wq, x.wk, wl.T, wl.H, wl.W, wl.theta, wl.eps, heads=heads, rows=rows,
                         mask=full)
     check_close(osp[idx][:, heads].float().cpu().numpy(), ref_s, "sparse v5 d128 sampled")
+
+
+def test_joint_d128_single_query_and_ragged_keys():
+    """nq = 1 against 131 keys (one full tile and a 3-key tail), positions in all three table sections."""
+    rng = np.random.default_rng(11)
+    bf = lambda a: f32_to_bf16_bits(a.astype(np.float32))
+    qb = bf(rng.standard_normal((1, 2, 128)))
+    kb, vb = bf(rng.standard_normal((131, 2, 128))), bf(rng.standard_normal((131, 2, 128)))
+    qp = np.array([[3, 9, 1]], dtype=np.int32)
+    kp = rng.integers(0, 12, (131, 3)).astype(np.int32)
+    wq = (1 + 0.1 * rng.standard_normal(128)).astype(np.float32)
+    wk = (1 + 0.1 * rng.standard_normal(128)).astype(np.float32)
+    t = lambda b: torch.from_numpy(b.view(np.int16)).to(DEV).view(torch.bfloat16)
+    o = dit.dit_attn_joint(t(qb), t(kb), t(vb), torch.from_numpy(wq).to(DEV), torch.from_numpy(wk).to(DEV),
+                           torch.from_numpy(qp).to(DEV), torch.from_numpy(kp).to(DEV), 12)
+    torch.cuda.synchronize()
+    ref = A.attention_joint(bf16_bits_to_f32(qb), bf16_bits_to_f32(kb), bf16_bits_to_f32(vb), wq, wk, qp, kp)
+    check_close(o.float().cpu().numpy(), ref, "joint d128 nq=1 nk=131")
