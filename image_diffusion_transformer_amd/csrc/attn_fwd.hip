@@ -525,20 +525,57 @@ __device__ __forceinline__ void tile_barrier() {
 // of the next tile's fragment image into the other LDS stage, then per 32-key sub-block: S MFMAs, softmax,
 // PV MFMAs.  One barrier per tile.  Block-sparse tiles are computed only for the query blocks whose
 // router block keeps them (activity mask QM of the wave's blocks).
+// S^T of sub-block kb with its first two K^ fragments already in registers (kp).
+template <int D, int QB, int QM>
+__device__ __forceinline__ void qk_block_pre(const uint16_t* T_, int kb, int lane, const bf16x8 (&qf)[QB][Head<D>::KS],
+                                             const bf16x8 (&kp)[2], f32x16 (&S)[QB]) {
+  constexpr int KS = Head<D>::KS;
+#pragma unroll
+  for (int qb = 0; qb < QB; ++qb) S[qb] = f32x16{};
+#pragma unroll
+  for (int ks = 0; ks < KS; ++ks) {
+    const bf16x8 ka = ks < 2 ? kp[ks] : *(const bf16x8*)(T_ + (kb * KS + ks) * kFrag + lane * 8);
+#pragma unroll
+    for (int qb = 0; qb < QB; ++qb)
+      if (((QM >> qb) & 1) != 0)
+        S[qb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka, qf[qb][ks], S[qb], 0, 0, 0);
+  }
+}
+
 template <int D, int QB, int QM, int MODE>
 __device__ __forceinline__ void tile_body(const uint16_t* T_, int lane, const bf16x8 (&qf)[QB][Head<D>::KS],
                                           f32x16 (&acc)[QB][Head<D>::DB], float (&m)[QB], float (&l)[QB],
                                           bool ragged, int key0, int N) {
+  constexpr int KS = Head<D>::KS;
+  if constexpr (MODE == kStatic) {
+    // The first two K^ fragments of each sub-block are read while the previous sub-block's S MFMAs
+    // drain, so a sub-block's S MFMAs start without an LDS wait (measured 0.6% on the dense layer;
+    // the online mode, with its longer softmax, was slower this way and keeps the plain order).
+    bf16x8 kp[2];
+    kp[0] = *(const bf16x8*)(T_ + 0 * kFrag + lane * 8);
+    kp[1] = *(const bf16x8*)(T_ + 1 * kFrag + lane * 8);
 #pragma unroll 1
-  for (int kb = 0; kb < BK / 32; ++kb) {
-    f32x16 S[QB];
-    qk_block<D, QB, QM>(T_, kb, lane, qf, S);
-    bf16x8 P[QB][2];
-    if constexpr (MODE == kStatic)
+    for (int kb = 0; kb < BK / 32; ++kb) {
+      f32x16 S[QB];
+      qk_block_pre<D, QB, QM>(T_, kb, lane, qf, kp, S);
+      const int nk = kb + 1 < BK / 32 ? kb + 1 : kb;   // the last sub-block re-reads its own (unused)
+      kp[0] = *(const bf16x8*)(T_ + (nk * KS + 0) * kFrag + lane * 8);
+      kp[1] = *(const bf16x8*)(T_ + (nk * KS + 1) * kFrag + lane * 8);
+      __builtin_amdgcn_sched_barrier(0);
+      bf16x8 P[QB][2];
       softmax_static<QB, QM>(S, l, P);
-    else
+      pv_block<D, QB, QM>(T_, kb, lane, P, acc);
+      asm volatile("" ::"v"(kp[0]), "v"(kp[1]));   // keeps the reads where they are issued
+    }
+  } else {
+#pragma unroll 1
+    for (int kb = 0; kb < BK / 32; ++kb) {
+      f32x16 S[QB];
+      qk_block<D, QB, QM>(T_, kb, lane, qf, S);
+      bf16x8 P[QB][2];
       softmax_online<Head<D>::DB, QB, QM>(S, ragged, key0 + kb * 32, N, lane, m, l, acc, P);
-    pv_block<D, QB, QM>(T_, kb, lane, P, acc);
+      pv_block<D, QB, QM>(T_, kb, lane, P, acc);
+    }
   }
 }
 
