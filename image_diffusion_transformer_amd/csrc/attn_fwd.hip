@@ -70,7 +70,13 @@ constexpr float kTau = 8.0f;  // lazy-rescale threshold, base-2 log units
 // Keys past the grid have zero K^ and V.  Head dim 96: 24 + 24 fragments (48 KB); 128: 32 + 32 (64 KB).
 constexpr int kFrag = 512;
 
-// Shape of the head-dim-128 workgroup: waves and 32-query blocks per wave.
+// Shape of the workgroups: waves and 32-query blocks per wave.
+#ifndef DIT_D96_NW
+#define DIT_D96_NW 8
+#endif
+#ifndef DIT_D96_QB
+#define DIT_D96_QB 2
+#endif
 #ifndef DIT_D128_NW
 #define DIT_D128_NW 8
 #endif
@@ -86,8 +92,8 @@ struct Head {
   static constexpr int VFRAG0 = 4 * KS;
   static constexpr int FRAGS = 4 * KS + 8 * DB;
   static constexpr int TILE = FRAGS * kFrag;         // bf16 elements of one tile image
-  static constexpr int NW = D == 96 ? 8 : DIT_D128_NW;   // waves per workgroup
-  static constexpr int QB = D == 96 ? 2 : DIT_D128_QB;   // 32-query blocks per wave
+  static constexpr int NW = D == 96 ? DIT_D96_NW : DIT_D128_NW;   // waves per workgroup
+  static constexpr int QB = D == 96 ? DIT_D96_QB : DIT_D128_QB;   // 32-query blocks per wave
   static constexpr int BQ = NW * QB * 32;                // queries per workgroup
   static constexpr int RS = rope_row_floats(D);       // floats per RoPE table row
   static constexpr int PAIRS0 = rope_width(D, 0) / 2, PAIRS1 = rope_width(D, 1) / 2;
