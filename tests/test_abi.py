@@ -243,3 +243,15 @@ def test_block_zero_tokens_queue_nothing(lib):
     assert _resid(lib, tokens=0) == B.DIT_OK
     assert _resid(lib, tokens=0, h=None, shift=None, scale=None) == B.DIT_OK
     assert _swiglu(lib, tokens=0) == B.DIT_OK
+
+
+def test_product_package_never_imports_the_oracle():
+    """The oracle is test infrastructure: importing and loading the product must not pull it in."""
+    import subprocess
+    import sys
+    root = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+    code = ("import sys; import image_diffusion_transformer_amd as d; d.load_library(); "
+            "bad = [m for m in sys.modules if m == 'oracle' or m.startswith('oracle.')]; "
+            "assert not bad, bad")
+    r = subprocess.run([sys.executable, "-c", code], cwd=root, capture_output=True, text=True, timeout=120)
+    assert r.returncode == 0, r.stderr[-2000:]
