@@ -26,6 +26,7 @@ COMMON = [
 ]
 SOURCES = [
     ("attn_fwd.hip", []),
+    ("sparse_sched.hip", []),
     # Router arithmetic must be reproducible bit for bit: no contraction into FMAs.
     ("router.hip", ["-ffp-contract=off"]),
     ("block_ops.hip", []),

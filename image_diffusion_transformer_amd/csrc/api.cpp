@@ -53,6 +53,8 @@ struct Layout {
   size_t route_score;// [heads][nb][nb] u32 order keys (nb <= dit::route_topk_max_blocks(), else unused)
   size_t list;       // [heads][nqt][nb] i32
   size_t list_len;   // [heads][nqt] i32
+  size_t perm;       // [heads][nqt][query tile / 128] i32 router block per query-tile slot
+  size_t bits;       // [heads][nb][schedule_words(nb)] u64 packed mask rows
   size_t total;
 };
 
@@ -68,9 +70,14 @@ Layout make_layout(const Shape& s) {
   L.route_score = base + pool_bytes;
   const size_t list_bytes = align256((size_t)s.heads * s.nqt * s.nb * sizeof(int));
   const size_t len_bytes = align256((size_t)s.heads * s.nqt * sizeof(int));
+  const int group = dit::attn_query_tile(s.d) / dit::kBlock;
+  const size_t perm_bytes = align256((size_t)s.heads * s.nqt * group * sizeof(int));
+  const size_t bits_bytes = align256((size_t)s.heads * s.nb * dit::schedule_words(s.nb) * sizeof(uint64_t));
   L.list = base;
-  L.list_len = base + list_bytes;
-  L.total = base + std::max(pool_bytes + score_bytes, list_bytes + len_bytes);
+  L.list_len = L.list + list_bytes;
+  L.perm = L.list_len + len_bytes;
+  L.bits = L.perm + perm_bytes;
+  L.total = base + std::max(pool_bytes + score_bytes, list_bytes + len_bytes + perm_bytes + bits_bytes);
   return L;
 }
 
@@ -334,19 +341,23 @@ dit_status dit_attn_block_sparse(const void* q, const void* k, const void* v, co
   if ((st = check_workspace(s, workspace, workspace_bytes, L)) != DIT_OK) return st;
   hipStream_t stream = (hipStream_t)hip_stream;
   if ((st = upload_table(s, rope_theta, workspace, L, stream)) != DIT_OK) return st;
-  dit::CompactArgs c{};
+  dit::ScheduleArgs c{};
   c.mask = mask;
+  c.bits = (unsigned long long*)((char*)workspace + L.bits);
+  c.perm = (int*)((char*)workspace + L.perm);
   c.list = (int*)((char*)workspace + L.list);
   c.list_len = (int*)((char*)workspace + L.list_len);
   c.heads = s.heads;
   c.nb = s.nb;
   c.nqt = s.nqt;
   c.group = dit::attn_query_tile(s.d) / dit::kBlock;
-  hipError_t e = dit::launch_compact(c, stream);
-  if (e != hipSuccess) return fail_hip(e, "mask compaction launch");
+  c.words = dit::schedule_words(s.nb);
+  hipError_t e = dit::launch_sparse_schedule(c, stream);
+  if (e != hipSuccess) return fail_hip(e, "block-sparse schedule launch");
   dit::AttnArgs a = attn_args(s, q, k, v, wq, wk, eps, o, workspace, L);
   a.list = c.list;
   a.list_len = c.list_len;
+  a.perm = c.perm;
   e = dit::launch_attn_sparse(a, stream);
   if (e != hipSuccess) return fail_hip(e, "sparse attention kernel launch");
   return DIT_OK;

@@ -13,9 +13,10 @@
 //    fragments (64 lanes x 16 bytes each; 48 KB at head dim 96, 64 KB at 128).
 //    The attention kernel then stages a KV tile with plain global->LDS copies and
 //    no vector ALU work, which leaves the VALU to the softmax.
-//  * Attention work is split per (head, query tile of NW*QB*32 tokens); the launch
-//    index is remapped so the workgroups resident on one XCD walk the same head's
-//    K/V and share its L2.
+//  * Attention work is split per (head, query tile of NW*QB*32 tokens); for dense
+//    calls the launch index is remapped so the workgroups resident on one XCD walk
+//    the same head's K/V and share its L2.  Block-sparse query tiles hold router
+//    blocks grouped by the overlap of their kept sets (sparse_sched.hip).
 //  * Each wave owns QB blocks of 32 queries (2 at head dim 96, 1 at 128, where
 //    the Q fragments and O accumulators of two blocks would not fit the 256
 //    registers of a wave).  Its Q rows are loaded once (two lanes per query, half
@@ -236,6 +237,21 @@ __device__ __forceinline__ int router_block(int wave, int qb) {
   return query_block<QB, SPARSE, NW>(wave, qb) >> 2;
 }
 
+// Token of the query that lane l32 holds in block qb of the wave.  Dense: the tile's consecutive
+// tokens.  Block-sparse: slot s of the tile holds the router block that the grouping pass put there
+// (a slot without one maps past the last query and is never loaded or stored).
+template <int D, bool SPARSE>
+__device__ __forceinline__ int query_token(const AttnArgs& a, int head, int qt, int wave, int qb, int l32) {
+  constexpr int QB = Head<D>::QB, BQ = Head<D>::BQ;
+  const int blk = query_block<QB, SPARSE, Head<D>::NW>(wave, qb);
+  if constexpr (SPARSE) {
+    const int rb = a.perm[((size_t)head * a.nqt + qt) * (BQ / BK) + (blk >> 2)];
+    return rb < 0 ? a.nq : rb * BK + (blk & 3) * 32 + l32;
+  } else {
+    return qt * BQ + blk * 32 + l32;
+  }
+}
+
 // Q fragments of the wave: load, RMSNorm, RoPE, scale by log2(e)/sqrt(d), pack to bf16 (once per query).
 template <int D, int QB, int BQ, bool SPARSE>
 __device__ __forceinline__ void load_q(const AttnArgs& a, int head, int qt, int wave, int lane,
@@ -244,7 +260,7 @@ __device__ __forceinline__ void load_q(const AttnArgs& a, int head, int qt, int 
   const int half = lane >> 5, l32 = lane & 31;
 #pragma unroll
   for (int qb = 0; qb < QB; ++qb) {
-    const int n = qt * BQ + query_block<QB, SPARSE, Head<D>::NW>(wave, qb) * 32 + l32;
+    const int n = query_token<D, SPARSE>(a, head, qt, wave, qb, l32);
     const bool live = n < a.nq;
     u32x4 raw[KS];
     const size_t base = ((size_t)(live ? n : 0) * a.g.heads + head) * D;
@@ -385,7 +401,7 @@ __device__ __forceinline__ void store_o(const AttnArgs& a, int head, int qt, int
   const int half = lane >> 5, l32 = lane & 31;
 #pragma unroll
   for (int qb = 0; qb < QB; ++qb) {
-    const int n = qt * BQ + query_block<QB, SPARSE, Head<D>::NW>(wave, qb) * 32 + l32;
+    const int n = query_token<D, SPARSE>(a, head, qt, wave, qb, l32);
     const float lt = pair_sum(l[qb]);
     const float inv = lt > 0.f ? 1.0f / lt : 0.f;
     if (n < a.nq) {
@@ -414,7 +430,12 @@ struct TileIter {
 
 template <bool SPARSE>
 __device__ __forceinline__ bool tile_iter(const AttnArgs& a, TileIter& ti) {
-  const int logical = (int)(blockIdx.x & 7) * a.per_xcd + (int)(blockIdx.x >> 3);
+  // Dense: XCD x (launch index mod 8) takes a contiguous run of (head, query tile) pairs, so the
+  // workgroups resident on one XCD walk one head's K/V in step and share its L2.  Block-sparse: the
+  // tiles of a head visit different KV subsets and drift apart, so L2 sharing is weak; consecutive
+  // launch indices keep the whole chip on about one head at a time instead, whose fragment image is
+  // then re-read from the last-level cache rather than HBM (3% faster on the 10 s video layer).
+  const int logical = SPARSE ? (int)blockIdx.x : (int)(blockIdx.x & 7) * a.per_xcd + (int)(blockIdx.x >> 3);
   if (logical >= a.total) return false;
   ti.head = logical / a.nqt;
   ti.qt = logical - ti.head * a.nqt;
@@ -665,36 +686,6 @@ __global__ void __launch_bounds__(64 * Head<D>::NW) attn_online_kernel(AttnArgs 
   attn_kernel_body<D, SPARSE, kOnline>(a, sKV);
 }
 
-// Block-sparse iteration lists: for each (head, query tile) the ascending KV blocks kept by any of the
-// tile's router blocks, each tagged with which of them keep it (bit b = router block b of the tile).
-__global__ void __launch_bounds__(256) compact_kernel(CompactArgs a) {
-  __shared__ int wave_tot[4];
-  const int tile = blockIdx.x;              // head * nqt + qt
-  const int head = tile / a.nqt, qt = tile - head * a.nqt;
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  int* out = a.list + (size_t)tile * a.nb;
-  int base = 0;
-  for (int j0 = 0; j0 < a.nb; j0 += 256) {
-    const int j = j0 + threadIdx.x;
-    int flags = 0;
-    if (j < a.nb)
-      for (int b = 0; b < a.group; ++b) {
-        const int i = qt * a.group + b;
-        if (i < a.nb && a.mask[((size_t)head * a.nb + i) * a.nb + j]) flags |= 1 << b;
-      }
-    const uint64_t bal = __builtin_amdgcn_ballot_w64(flags != 0);
-    const int before = __builtin_popcountll(bal & ((1ull << lane) - 1ull));
-    if (lane == 0) wave_tot[wave] = __builtin_popcountll(bal);
-    __syncthreads();
-    int off = base;
-    for (int w = 0; w < wave; ++w) off += wave_tot[w];
-    if (flags) out[off + before] = j | (flags << 24);
-    base += wave_tot[0] + wave_tot[1] + wave_tot[2] + wave_tot[3];
-    __syncthreads();
-  }
-  if (threadIdx.x == 0) a.list_len[tile] = base;
-}
-
 template <int D, bool SPARSE>
 hipError_t launch_attn(const AttnArgs& a, hipStream_t s) {
   hipLaunchKernelGGL(kv_prep_kernel<D>, dim3(a.nb, a.g.heads), dim3(256), 0, s, a);
@@ -719,11 +710,6 @@ hipError_t launch_attn_dense(const AttnArgs& a, hipStream_t s) {
 }
 hipError_t launch_attn_sparse(const AttnArgs& a, hipStream_t s) {
   return a.head_dim == 128 ? launch_attn<128, true>(a, s) : launch_attn<96, true>(a, s);
-}
-
-hipError_t launch_compact(const CompactArgs& a, hipStream_t s) {
-  hipLaunchKernelGGL(compact_kernel, dim3(a.heads * a.nqt), dim3(256), 0, s, a);
-  return hipGetLastError();
 }
 
 }  // namespace dit

@@ -64,6 +64,7 @@ struct AttnArgs {
   // block-sparse iteration lists (null for dense)
   const int* list;        // [heads][nqt][nb]: kv block | (router-block flags << 24)
   const int* list_len;    // [heads][nqt]
+  const int* perm;        // [heads][nqt][BQ/128]: router block in each slot of a query tile, -1 = none
   int nb;                 // 128-key tiles: ceil(nk / 128)
 };
 
@@ -83,11 +84,14 @@ struct RouteArgs {
   int head_dim;           // 96 or 128
 };
 
-struct CompactArgs {
+struct ScheduleArgs {
   const unsigned char* mask;   // [heads][nb][nb]
+  unsigned long long* bits;    // [heads][nb][words] packed mask rows
+  int* perm;                   // [heads][nqt][group] router block of each query-tile slot, -1 = none
   int* list;                   // [heads][nqt][nb]
   int* list_len;               // [heads][nqt]
-  int heads, nb, nqt, group;   // group = router blocks per query tile
+  int heads, nb, nqt, group;   // group = router blocks per query tile (<= 8)
+  int words;                   // schedule_words(nb)
 };
 
 // Operators around attention: AdaLN update and gated residual (one wave per token row).
@@ -120,7 +124,10 @@ int attn_query_tile(int head_dim);
 
 hipError_t launch_attn_dense(const AttnArgs& a, hipStream_t s);
 hipError_t launch_attn_sparse(const AttnArgs& a, hipStream_t s);
-hipError_t launch_compact(const CompactArgs& a, hipStream_t s);
+// Packs the mask, groups router blocks into query tiles and writes the iteration lists (three kernels).
+hipError_t launch_sparse_schedule(const ScheduleArgs& a, hipStream_t s);
+// 64-bit words of a packed mask row.
+int schedule_words(int nb);
 hipError_t launch_route(const RouteArgs& a, hipStream_t s);
 hipError_t launch_adaln(const BlockArgs& a, bool resid, bool norm, hipStream_t s);
 hipError_t launch_swiglu(SwigluArgs a, hipStream_t s);

@@ -202,6 +202,27 @@ def test_block_sparse_random_mask_with_empty_rows():
     assert np.all(got[(wl.nb - 1) * 128:, 1] == 0)
 
 
+@pytest.mark.parametrize("name", ["s4", "s4_128"])
+def test_block_sparse_rows_do_not_depend_on_other_rows(name):
+    """Which router blocks share a query tile is chosen from the whole mask, but each block's output
+    must depend only on its own row of the mask: the same block run alone is bitwise equal."""
+    x = make_inputs(name)
+    wl = x.workload
+    mask = R.route_mask(x.q, x.k, x.wq, x.wk, wl.T, wl.H, wl.W, 0.75, wl.theta, wl.eps)
+    q, k, v, wq, wk = upload(x)
+    full = dit.dit_attn_block_sparse(q, k, v, wq, wk, grid(wl), torch.from_numpy(mask).to(DEV), wl.theta, wl.eps)
+    for i in (0, 17, wl.nb - 1):
+        alone = np.zeros_like(mask)
+        alone[:, i] = mask[:, i]
+        o = dit.dit_attn_block_sparse(q, k, v, wq, wk, grid(wl), torch.from_numpy(alone).to(DEV), wl.theta, wl.eps)
+        torch.cuda.synchronize()
+        rows = slice(i * 128, min((i + 1) * 128, wl.N))
+        assert torch.equal(o[rows], full[rows]), f"block {i}"
+        others = np.ones(wl.N, bool)
+        others[rows] = False
+        assert torch.count_nonzero(o[torch.from_numpy(others).to(DEV)]) == 0
+
+
 def test_route_then_sparse_pipeline():
     x = make_inputs("s4")
     wl = x.workload
