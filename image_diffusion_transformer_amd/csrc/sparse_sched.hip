@@ -111,7 +111,9 @@ __global__ void __launch_bounds__(kWindow) group_kernel(ScheduleArgs a) {
         pick = seed + 1 + (kWindow - 1 - (best & 0xff));
         if (tid < W) uni[tid] |= ring[tid][pick & (kWindow - 1)];
       } else {
-        // nothing left in the window: the lowest block still free anywhere (or none)
+        // Nothing left in the window: the lowest block still free anywhere (none once every block is
+        // placed).  Earlier tiles, whose windows end below this one's, can fill at most its first 255
+        // blocks, so this happens only after the current tile itself took the 256th.
         pick = lowest_free(seed + 1);
         __syncthreads();                           // every thread has read `used` before it changes
         if (pick >= 0 && tid < W) uni[tid] |= rows[(size_t)pick * W + tid];
