@@ -10,7 +10,8 @@
 // visited tile do work.  The grouping pass therefore builds each query tile greedily: the lowest block
 // not yet placed, then, G-1 times, the not-yet-placed block among the next kWindow blocks whose kept set
 // overlaps the tile's running union most (ties: the lowest block).  On routed video masks this cuts the
-// visited tiles by about 15%.
+// visited tiles by about 15%.  Segments of kSegment consecutive blocks are grouped independently (one
+// workgroup each), which shortens the sequential chain; it costs about 0.3% more visited tiles.
 #include "dit_internal.h"
 
 namespace dit {
@@ -18,6 +19,7 @@ namespace {
 
 constexpr int kWindow = 256;          // candidate blocks per greedy step (one per thread)
 constexpr int kRingWords = 64;        // greedy grouping up to 4096 blocks (LDS ring of 256 x 64 words)
+constexpr int kSegment = 512;         // blocks grouped by one workgroup (a multiple of every group size)
 constexpr int kMaxWords = 512;        // 64-bit words of a packed row (32768 blocks)
 
 // Packed mask rows: bit j of word w of row i is mask[i][64 w + j].  One wave per row.
@@ -46,47 +48,55 @@ __device__ __forceinline__ int wave_max(int v) {
              max(__builtin_amdgcn_readlane(v, 32), __builtin_amdgcn_readlane(v, 48)));
 }
 
-// One workgroup of four waves per head.  perm[head][qt * G + s] = router block in slot s of query tile
-// qt, -1 = none.  Thread t keeps, in slot t of an LDS ring, the packed row of the window block congruent
-// to t mod 256, so a greedy step reads candidate rows from LDS only; a row enters the ring once, when the
-// window reaches it.  Above 4096 blocks the tiles take consecutive blocks.
+// One workgroup of four waves per (segment, head): blocks b0 .. b1-1 fill query tiles b0/G, b0/G + 1, ...
+// perm[head][qt * G + s] = router block in slot s of query tile qt, -1 = none.  Thread t keeps, in slot
+// t of an LDS ring, the packed row of the window block congruent to t mod 256, so a greedy step reads
+// candidate rows from LDS only; a row enters the ring once, when the window reaches it.  Above 4096
+// blocks the tiles take consecutive blocks.
 __global__ void __launch_bounds__(kWindow) group_kernel(ScheduleArgs a) {
   __shared__ unsigned long long ring[kRingWords][kWindow];   // word-major: lanes read consecutive words
   __shared__ unsigned long long used[kRingWords];            // placed blocks
   __shared__ unsigned long long uni[kRingWords];             // union of the current tile's kept sets
   __shared__ int red[kWindow / 64];
-  const int head = blockIdx.x, tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int head = blockIdx.y, tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int nb = a.nb, W = a.words, G = a.group;
+  const int b0 = blockIdx.x * kSegment, b1 = min(nb, b0 + kSegment);
+  const int g0 = b0 / G, g1 = g0 + (b1 - b0 + G - 1) / G;     // this segment's query tiles
   int* perm = a.perm + (size_t)head * a.nqt * G;
   if (W > kRingWords) {
-    for (int i = tid; i < a.nqt * G; i += kWindow) perm[i] = i < nb ? i : -1;
+    for (int i = g0 * G + tid; i < g1 * G; i += kWindow) perm[i] = i < b1 ? i : -1;
     return;
   }
   const unsigned long long* rows = a.bits + (size_t)head * nb * W;
-  if (tid < W) used[tid] = 0;
+  // blocks outside the segment (and past the grid) count as placed
+  for (int w = tid; w < W; w += kWindow) {
+    unsigned long long outside = 0;
+    if (64 * w < b0) outside |= b0 - 64 * w >= 64 ? ~0ull : (1ull << (b0 - 64 * w)) - 1ull;
+    if (64 * w + 64 > b1) outside |= b1 <= 64 * w ? ~0ull : ~0ull << (b1 - 64 * w);
+    used[w] = outside;
+  }
   // lowest block at or after `from` that is not placed yet; -1 if none
   auto lowest_free = [&](int from) {
     for (int w = from >> 6; w < W; ++w) {
       unsigned long long f = ~used[w];
-      if (w == W - 1 && (nb & 63)) f &= (1ull << (nb & 63)) - 1ull;
       if (w == (from >> 6)) f &= ~0ull << (from & 63);
       if (f) return 64 * w + __builtin_ctzll(f);
     }
     return -1;
   };
-  int seed = 0, held = -1;
+  int seed = b0, held = -1;
   __syncthreads();
-  for (int g = 0; g < a.nqt; ++g) {
+  for (int g = g0; g < g1; ++g) {
     // Every thread finds the same seed: `used` is not written again until after the next barrier.
     seed = lowest_free(seed);
-    if (seed < 0) {                                // cannot happen while g < nqt; keeps the slots defined
+    if (seed < 0) {                                // cannot happen while g < g1; keeps the slots defined
       if (tid < G) perm[g * G + tid] = -1;
       continue;
     }
     const int c = seed + 1 + ((tid - seed - 1) & (kWindow - 1));   // window block held in slot tid
     if (c != held) {
       held = c;
-      if (c < nb)
+      if (c < b1)
         for (int i = 0; i < W; ++i) ring[i][tid] = rows[(size_t)c * W + i];
     }
     if (tid < W) uni[tid] = rows[(size_t)seed * W + tid];
@@ -94,7 +104,7 @@ __global__ void __launch_bounds__(kWindow) group_kernel(ScheduleArgs a) {
     __syncthreads();
     for (int s = 1; s < G; ++s) {
       int key = -1;
-      if (c < nb && !((used[c >> 6] >> (c & 63)) & 1ull)) {
+      if (c < b1 && !((used[c >> 6] >> (c & 63)) & 1ull)) {
         int ov = 0;
 #pragma unroll 8
         for (int i = 0; i < W; ++i) ov += __builtin_popcountll(ring[i][tid] & uni[i]);
@@ -111,9 +121,9 @@ __global__ void __launch_bounds__(kWindow) group_kernel(ScheduleArgs a) {
         pick = seed + 1 + (kWindow - 1 - (best & 0xff));
         if (tid < W) uni[tid] |= ring[tid][pick & (kWindow - 1)];
       } else {
-        // Nothing left in the window: the lowest block still free anywhere (none once every block is
-        // placed).  Earlier tiles, whose windows end below this one's, can fill at most its first 255
-        // blocks, so this happens only after the current tile itself took the 256th.
+        // Nothing left in the window: the lowest block of the segment still free (none once every
+        // block is placed).  Earlier tiles, whose windows end below this one's, can fill at most its
+        // first 255 blocks, so this happens only after the current tile itself took the 256th.
         pick = lowest_free(seed + 1);
         __syncthreads();                           // every thread has read `used` before it changes
         if (pick >= 0 && tid < W) uni[tid] |= rows[(size_t)pick * W + tid];
@@ -171,7 +181,7 @@ hipError_t launch_sparse_schedule(const ScheduleArgs& a, hipStream_t s) {
   hipLaunchKernelGGL(mask_pack_kernel, dim3((a.nb + 3) / 4, a.heads), dim3(256), 0, s, a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(group_kernel, dim3(a.heads), dim3(kWindow), 0, s, a);
+  hipLaunchKernelGGL(group_kernel, dim3((a.nb + kSegment - 1) / kSegment, a.heads), dim3(kWindow), 0, s, a);
   if ((e = hipGetLastError()) != hipSuccess) return e;
   hipLaunchKernelGGL(compact_kernel, dim3(a.heads * a.nqt), dim3(256), 0, s, a);
   return hipGetLastError();
