@@ -4,13 +4,15 @@ oracle (same tolerances as the other attention tests: max-abs 2e-2, relative L2 
 The schedule puts each 512-token query tile's four router blocks together greedily: the lowest block not
 yet placed, then the block among the next 256 that overlaps the tile's kept union most.  When every one
 of those 256 blocks is already placed, it takes the lowest free block anywhere; above 4096 blocks it
-takes consecutive blocks.  The output must not depend on any of this."""
+takes consecutive blocks.  The output must not depend on any of this; the running-max kernel must
+handle the grouped tiles as the static-shift one does."""
 import numpy as np
 import pytest
 import torch
 
 import image_diffusion_transformer_amd as dit
 from oracle import attention as A
+from oracle import router as R
 from synth import custom_workload, make_inputs
 
 pytestmark = pytest.mark.gpu
@@ -94,3 +96,21 @@ def test_consecutive_tiles_above_4096_blocks():
     ref = A.attention(x.q, x.k, x.v, x.wq, x.wk, wl.T, wl.H, wl.W, wl.theta, wl.eps, rows=rows, mask=mask)
     check_close(got, ref, "sparse nb=4100")
     assert np.all(got[128:256] == 0)
+
+
+@pytest.mark.parametrize("name", ["s4", "s4_128"])
+def test_block_sparse_online_softmax_weights(name):
+    """Norm weights whose logit bound exceeds the static-shift limit: the running-max kernel runs on the
+    grouped tiles (ragged last block included), router mask from the oracle."""
+    x = make_inputs(name)
+    wl = x.workload
+    wq = x.wq.copy()
+    wq[5] = 4.0
+    mask = R.route_mask(x.q, x.k, wq, x.wk, wl.T, wl.H, wl.W, 0.75, wl.theta, wl.eps)
+    q, k, v, _, wk = upload(x)
+    print(f"case sparse online {name}", flush=True)
+    o = dit.dit_attn_block_sparse(q, k, v, torch.from_numpy(wq).to(DEV), wk, (wl.T, wl.H, wl.W),
+                                  torch.from_numpy(mask).to(DEV), wl.theta, wl.eps)
+    torch.cuda.synchronize()
+    ref = A.attention(x.q, x.k, x.v, wq, x.wk, wl.T, wl.H, wl.W, wl.theta, wl.eps, mask=mask)
+    check_close(o.float().cpu().numpy(), ref, f"sparse online {name}")
