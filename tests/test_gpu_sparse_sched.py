@@ -114,3 +114,23 @@ def test_block_sparse_online_softmax_weights(name):
     torch.cuda.synchronize()
     ref = A.attention(x.q, x.k, x.v, wq, x.wk, wl.T, wl.H, wl.W, wl.theta, wl.eps, mask=mask)
     check_close(o.float().cpu().numpy(), ref, f"sparse online {name}")
+
+
+@pytest.mark.parametrize("H,nb", [(513, 513), (1024, 1024)])
+def test_segment_boundaries(H, nb):
+    """Router blocks are grouped in independent segments of 512: 513 blocks leave a segment of one block
+    (a tile with three empty slots), 1024 give two full segments."""
+    wl = custom_workload(1, H, 128, 2, seed=44)
+    assert wl.nb == nb
+    x = make_inputs(wl)
+    q, k, v, wq, wk = upload(x)
+    mask = R.route_mask(x.q, x.k, x.wq, x.wk, wl.T, wl.H, wl.W, 0.75, wl.theta, wl.eps)
+    print(f"case sparse segments nb={nb}", flush=True)
+    o = dit.dit_attn_block_sparse(q, k, v, wq, wk, (wl.T, wl.H, wl.W), torch.from_numpy(mask).to(DEV),
+                                  wl.theta, wl.eps)
+    torch.cuda.synchronize()
+    blocks = [0, 255, 510, 511, 512, nb - 1]
+    rows = np.concatenate([np.arange(b * 128, (b + 1) * 128) for b in sorted(set(blocks))])
+    got = o[torch.from_numpy(rows).to(DEV)].float().cpu().numpy()
+    ref = A.attention(x.q, x.k, x.v, x.wq, x.wk, wl.T, wl.H, wl.W, wl.theta, wl.eps, rows=rows, mask=mask)
+    check_close(got, ref, f"sparse segments nb={nb}")
