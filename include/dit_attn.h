@@ -58,7 +58,8 @@ typedef enum {
 
 /* Bytes of device workspace that dense, route and block_sparse need for this
  * shape (enough for any of the three; about 2 * N * heads * head_dim * 2 bytes
- * for the K^/V fragment images plus the router's or the sparse lists' share).
+ * for the K^/V fragment images plus the router's or the block-sparse schedule's
+ * share: iteration lists, grouping table and the mask packed to bits).
  * Returns 0 if the shape is invalid. */
 size_t dit_attn_workspace_bytes(int T, int H, int W, int heads, int head_dim, int block);
 
