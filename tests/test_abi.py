@@ -56,6 +56,9 @@ def test_workspace_bytes(lib):
     assert big < 4100 * 48 * 1024 + 2 * 4100 * 96 * 4 + 4100 * 4100 * 4
     assert n >= 56 * -(-N // 512) * nb * 4                  # sparse: KV lists per 512-token query tile
     assert n >= 56 * nb * 48 * 1024 + 56 * -(-N // 512) * nb * 4   # K^/V fragment images + sparse lists
+    nqt, words = -(-N // 512), -(-nb // 64)
+    sched = 56 * nqt * nb * 4 + 56 * nqt * 4 + 56 * nqt * 4 * 4 + 56 * nb * words * 8   # lists, counts, slots, bits
+    assert n >= 56 * nb * 48 * 1024 + sched
     assert dit.dit_attn_workspace_bytes(31, 48, 84, 56, 64) == 0    # head_dim 64 unsupported
     n128 = dit.dit_attn_workspace_bytes(31, 48, 84, 42, 128)        # 42 heads x 128: 64 KB tile images
     assert n128 >= 42 * nb * 64 * 1024 + 2 * 42 * nb * 128 * 4 + 42 * nb * nb * 4
