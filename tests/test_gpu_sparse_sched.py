@@ -134,3 +134,27 @@ def test_segment_boundaries(H, nb):
     got = o[torch.from_numpy(rows).to(DEV)].float().cpu().numpy()
     ref = A.attention(x.q, x.k, x.v, x.wq, x.wk, wl.T, wl.H, wl.W, wl.theta, wl.eps, rows=rows, mask=mask)
     check_close(got, ref, f"sparse segments nb={nb}")
+
+
+@pytest.mark.parametrize("d", [96, 128])
+@pytest.mark.parametrize("T,H,W,heads", [(1, 1, 1, 1), (1, 1, 5, 2), (1, 1, 257, 3), (3, 7, 11, 5)])
+def test_block_sparse_edge_shapes(T, H, W, heads, d):
+    """A single token, one short block, a ragged third block, several heads: random masks with an empty
+    row in head 0 (that block's output must be exactly 0) and rows kept in full elsewhere."""
+    wl = custom_workload(T, H, W, heads, seed=7 * T + H + W, head_dim=d)
+    x = make_inputs(wl)
+    q, k, v, wq, wk = upload(x)
+    rng = np.random.default_rng(T * 100 + W)
+    mask = (rng.random((heads, wl.nb, wl.nb)) < 0.5).astype(np.uint8)
+    mask[:, np.arange(wl.nb), np.arange(wl.nb)] = 1
+    if wl.nb > 1:
+        mask[0, 0] = 0
+    print(f"case sparse edge {T}x{H}x{W} heads={heads} d={d}", flush=True)
+    o = dit.dit_attn_block_sparse(q, k, v, wq, wk, (T, H, W), torch.from_numpy(mask).to(DEV), wl.theta, wl.eps)
+    torch.cuda.synchronize()
+    assert o.shape == (wl.N, heads, d)
+    got = o.float().cpu().numpy()
+    ref = A.attention(x.q, x.k, x.v, x.wq, x.wk, T, H, W, wl.theta, wl.eps, mask=mask)
+    check_close(got, ref, f"sparse edge {T}x{H}x{W}x{heads} d={d}")
+    if wl.nb > 1:
+        assert np.all(got[:128, 0] == 0)
