@@ -189,29 +189,37 @@ __device__ __forceinline__ u32x4 norm_rope_chunk(u32x4 raw, float r, float scale
   return out;
 }
 
-// Softmax modes.  QK-RMSNorm bounds every logit: |q^ . k^| / sqrt(d) <= sqrt(d) max|w_q| max|w_k|
-// (RoPE preserves norms).  When that bound, in base-2 units, is at most kStaticBound, exp2(S) with
-// no shift can neither overflow nor underflow for any input, and the shift cancels in O / rowsum:
-// no running max, no subtraction, no rescale.  Otherwise the online (running-max) softmax runs.
+// Softmax modes.  QK-RMSNorm bounds every logit.  RoPE rotates each channel pair (2i, 2i+1) rigidly, so
+// pair i of q^ . k^ is at most |a_i| |b_i|, with a_i the normalised q pair times its weights:
+// |a_i| <= u_i |x_i|, u_i = max(|w_q,2i|, |w_q,2i+1|) (v_i likewise for k).  Summing and Cauchy-Schwarz
+// over the pairs (|x| <= sqrt(d) after the norm): |q^ . k^| / sqrt(d) <= sqrt(d) max_i u_i v_i, never
+// looser than sqrt(d) max|w_q| max|w_k|.  When that bound, in base-2 units, is at most kStaticBound,
+// exp2(S) with no shift can neither overflow nor underflow for any input, and the shift cancels in
+// O / rowsum: no running max, no subtraction, no rescale.  Otherwise the online (running-max) softmax
+// runs.
 enum SoftmaxMode { kStatic = 0, kOnline = 1 };
 constexpr float kStaticBound = 48.0f;
 
 template <int D>
 __device__ __forceinline__ bool static_bound_holds(const AttnArgs& a, int lane) {
-  float mq = 0.f, mk = 0.f;
-  for (int i = lane; i < D; i += 64) {
-    mq = fmaxf(mq, fabsf(a.wq[i]));
-    mk = fmaxf(mk, fabsf(a.wk[i]));
+  float m = 0.f;
+  int bad = 0;                                     // a NaN weight sends the call to the online kernel
+  for (int i = lane; i < D / 2; i += 64) {
+    const float u = fmaxf(fabsf(a.wq[2 * i]), fabsf(a.wq[2 * i + 1]));
+    const float v = fmaxf(fabsf(a.wk[2 * i]), fabsf(a.wk[2 * i + 1]));
+    bad |= (a.wq[2 * i] != a.wq[2 * i]) | (a.wq[2 * i + 1] != a.wq[2 * i + 1]) |
+           (a.wk[2 * i] != a.wk[2 * i]) | (a.wk[2 * i + 1] != a.wk[2 * i + 1]);
+    m = fmaxf(m, u * v);
   }
 #pragma unroll
   for (int o = 32; o >= 1; o >>= 1) {
-    mq = fmaxf(mq, __shfl_xor(mq, o));
-    mk = fmaxf(mk, __shfl_xor(mk, o));
+    m = fmaxf(m, __shfl_xor(m, o));
+    bad |= __shfl_xor(bad, o);
   }
-  // |q^|, |k^| <= sqrt(d) max|w| (RMS <= 1 after the norm); 1.02 covers rsq, rotation and bf16 rounding.
+  // 1.02 covers the approximate reciprocal square root, the rotation and the bf16 rounding of q^, k^.
   const float sqrt_d = D == 96 ? 9.797958971132712f : 11.313708498984761f;
-  const float bound = 1.4426950408889634f * sqrt_d * mq * mk * 1.02f;
-  return bound <= kStaticBound;   // false for NaN weights
+  const float bound = 1.4426950408889634f * sqrt_d * m * 1.02f;
+  return !bad && bound <= kStaticBound;            // false for infinite weights too
 }
 
 // Query block (32 queries) of the workgroup's tile that block qb of a wave holds.  Dense: wave w holds

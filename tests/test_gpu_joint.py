@@ -87,8 +87,8 @@ def test_joint_single_query_and_ragged_keys():
 
 def test_joint_online_softmax_weights():
     """Norm weights whose logit bound exceeds the static-shift limit take the running-max kernel.  One
-    large channel weight (4.0) lifts the bound sqrt(96) max|w_q| max|w_k| log2(e) above 48 while the
-    typical logit stays of the usual size."""
+    large channel weight (4.0) lifts the bound log2(e) sqrt(96) max_i u_i v_i (u_i, v_i the larger
+    |weight| of channel pair i of w_q, w_k) above 48 while the typical logit stays of the usual size."""
     x = make_joint_inputs("j_small")
     wl = x.workload
     wq = x.wq.copy()

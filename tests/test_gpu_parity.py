@@ -108,12 +108,28 @@ def aligned_keys(x, wl, qrows, krows, head):
     return f32_to_bf16_bits((u / x.wk).astype(np.float32))
 
 
-def test_dense_running_max_rescale():
+def static_shift_bound(wq, wk, d=96):
+    """The kernels' test for the static-shift softmax, restated: the base-2 logit bound
+    log2(e) sqrt(d) max_i u_i v_i (u_i, v_i the larger |weight| of channel pair i of w_q, w_k), with
+    the kernels' 2% margin; at most 48 selects the static kernel."""
+    u = np.maximum(np.abs(wq[0::2]), np.abs(wq[1::2])).astype(np.float64)
+    v = np.maximum(np.abs(wk[0::2]), np.abs(wk[1::2])).astype(np.float64)
+    return np.log2(np.e) * np.sqrt(d) * float(np.max(u * v)) * 1.02
+
+
+@pytest.mark.parametrize("big_weight", [False, True])
+def test_dense_running_max_rescale(big_weight):
     """Queries 0..63 meet keys aligned with them (logit ~ sqrt(96) ~ 9.4) only in the second tile,
-    well above every earlier block max (~3): the running max must move by more than the lazy
-    threshold there, rescaling O and the row sum."""
+    well above every earlier block max (~3).  With one large query weight (channel pair 0) the logit
+    bound exceeds the static-shift limit, the running-max kernel runs, and its max must move by more
+    than the lazy threshold there, rescaling O and the row sum.  With standard weights the static
+    kernel runs the same case."""
     wl = custom_workload(1, 5, 40, 2, seed=41, smooth=False)        # N = 200: keys 136..199 aligned
     x = make_inputs(wl)
+    if big_weight:
+        x.wq = x.wq.copy()
+        x.wq[0] = 4.0
+    assert (static_shift_bound(x.wq, x.wk) > 48) == big_weight
     N = wl.N
     for hd in range(wl.heads):
         x.k.bits[N - 64:, hd, :] = aligned_keys(x, wl, np.arange(64), np.arange(N - 64, N), hd)
@@ -121,7 +137,7 @@ def test_dense_running_max_rescale():
     assert np.all(L[np.arange(64), N - 64 + np.arange(64)] - L[:, :N - 64].max(axis=1) > 8 / np.log2(np.e))
     got = as_np(run_dense(x))
     ref = A.attention(x.q, x.k, x.v, x.wq, x.wk, wl.T, wl.H, wl.W)
-    check_close(got, ref, "dense late max")
+    check_close(got, ref, f"dense late max ({'running max' if big_weight else 'static shift'})")
 
 
 def test_dense_deterministic():
