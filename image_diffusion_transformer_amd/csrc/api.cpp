@@ -46,6 +46,9 @@ struct Shape {
 
 bool head_dim_ok(int d) { return d == 96 || d == 128; }
 
+// Several kernels index heads with a launch grid dimension other than x, which holds at most 65535.
+constexpr int kMaxHeads = 65535;
+
 struct Layout {
   size_t tab;        // RoPE table [(T+H+W)][rope_row_floats(d)] f32
   size_t kvf;        // K^ / V^T fragment images [heads][nb] x tile_image_bytes(d) (dense and block-sparse)
@@ -89,6 +92,7 @@ dit_status check_shape(int T, int H, int W, int heads, int head_dim, Shape& s) {
     return fail(DIT_ERR_INVALID_ARG, "grid and heads must be >= 1 (T=%d H=%d W=%d heads=%d)", T, H, W, heads);
   if (!head_dim_ok(head_dim))
     return fail(DIT_ERR_UNSUPPORTED, "head_dim %d is not supported (96 or 128)", head_dim);
+  if (heads > kMaxHeads) return fail(DIT_ERR_UNSUPPORTED, "heads %d exceeds %d", heads, kMaxHeads);
   const long long N = (long long)T * H * W;
   if (N * heads * head_dim > 2147483647ll)
     return fail(DIT_ERR_UNSUPPORTED, "N*heads*head_dim = %lld exceeds 2^31-1 elements", N * heads * head_dim);
@@ -234,6 +238,7 @@ dit_status check_joint_shape(int nq, int nk, int heads, int head_dim, int max_po
     return fail(DIT_ERR_INVALID_ARG, "token counts and heads must be >= 1 (nq=%d nk=%d heads=%d)", nq, nk, heads);
   if (!head_dim_ok(head_dim))
     return fail(DIT_ERR_UNSUPPORTED, "head_dim %d is not supported (96 or 128)", head_dim);
+  if (heads > kMaxHeads) return fail(DIT_ERR_UNSUPPORTED, "heads %d exceeds %d", heads, kMaxHeads);
   if (max_pos < 1) return fail(DIT_ERR_INVALID_ARG, "max_pos must be >= 1 (got %d)", max_pos);
   if (max_pos > kMaxPos) return fail(DIT_ERR_UNSUPPORTED, "max_pos %d exceeds %d", max_pos, kMaxPos);
   const long long big = std::max(nq, nk);

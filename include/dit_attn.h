@@ -28,7 +28,8 @@
  *    of width c the pairs are (2i, 2i+1) at angle pos * rope_theta^(-2i/c); the
  *    pair (a, b) becomes (a cos - b sin, a sin + b cos).  V is untouched.
  *  - Attention: O = softmax(Q^ K^T / sqrt(head_dim)) V, every query sees every key.
- *  - head_dim must be 96 or 128 and block 128 (DIT_ERR_UNSUPPORTED otherwise).
+ *  - head_dim must be 96 or 128, block 128 and heads at most 65535
+ *    (DIT_ERR_UNSUPPORTED otherwise).
  *  - All pointers are owned by the caller.  The library allocates no device
  *    memory; scratch space comes from `workspace` (see dit_attn_workspace_bytes).
  *  - Every call is asynchronous on `hip_stream` (a hipStream_t; NULL means the

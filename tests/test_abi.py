@@ -104,6 +104,7 @@ def _sparse(lib, **kw):
     (dict(heads=-1), B.DIT_ERR_INVALID_ARG, "grid"),
     (dict(d=64), B.DIT_ERR_UNSUPPORTED, "head_dim"),
     (dict(T=4000, H=4000, W=4), B.DIT_ERR_UNSUPPORTED, "exceeds"),
+    (dict(T=1, H=1, W=1, heads=70000), B.DIT_ERR_UNSUPPORTED, "heads 70000 exceeds"),
     (dict(theta=0.0), B.DIT_ERR_INVALID_ARG, "rope_theta"),
     (dict(theta=float("inf")), B.DIT_ERR_INVALID_ARG, "rope_theta"),
     (dict(eps=-1.0), B.DIT_ERR_INVALID_ARG, "eps"),
@@ -177,6 +178,7 @@ def _joint(lib, **kw):
     (dict(maxp=(1 << 20) + 1), B.DIT_ERR_UNSUPPORTED, "max_pos"),
     (dict(d=64), B.DIT_ERR_UNSUPPORTED, "head_dim"),
     (dict(nk=30_000_000), B.DIT_ERR_UNSUPPORTED, "exceeds"),
+    (dict(nq=1, nk=1, heads=70000), B.DIT_ERR_UNSUPPORTED, "heads 70000 exceeds"),
     (dict(theta=-1.0), B.DIT_ERR_INVALID_ARG, "rope_theta"),
     (dict(ws=None), B.DIT_ERR_WORKSPACE, "workspace"),
     (dict(wsb=64), B.DIT_ERR_WORKSPACE, "need"),
