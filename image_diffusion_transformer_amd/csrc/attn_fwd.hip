@@ -538,9 +538,8 @@ __device__ __forceinline__ void lds_copy16(const void* src, __attribute__((addre
 
 // This wave's share (fragments FPW*w .. FPW*w + FPW-1, FPW = FRAGS / 8) of one tile's fragment image,
 // copied global -> LDS without passing through registers: lane l of each copy moves the 16 bytes of lane
-// slot l.  ASM: the copies go through lds_copy16 (1-2% faster on the dense layer,
-// 3% slower on the block-sparse one, which keeps the builtin).
-template <int D, bool ASM>
+// slot l.
+template <int D>
 __device__ __forceinline__ void dma_tile(const uint16_t* src, int wave, int lane, uint16_t* dst) {
   typedef __attribute__((address_space(3))) void lds_void;
   constexpr int FPW = Head<D>::FRAGS / Head<D>::NW;
@@ -548,11 +547,7 @@ __device__ __forceinline__ void dma_tile(const uint16_t* src, int wave, int lane
 #pragma unroll
   for (int c = 0; c < FPW; ++c) {
     const int f = FPW * wave + c;
-    if constexpr (ASM)
-      lds_copy16((const void*)(src + f * kFrag + lane * 8), (lds_void*)(dst + f * kFrag));
-    else
-      __builtin_amdgcn_global_load_lds((const void*)(src + f * kFrag + lane * 8), (lds_void*)(dst + f * kFrag), 16,
-                                       0, 0);
+    lds_copy16((const void*)(src + f * kFrag + lane * 8), (lds_void*)(dst + f * kFrag));
   }
 }
 
@@ -645,7 +640,7 @@ __device__ __forceinline__ void attn_kernel_body(const AttnArgs& a, uint16_t* sK
 #pragma unroll
   for (int qb = 0; qb < QB; ++qb) rbit[qb] = router_block<QB, SPARSE, Head<D>::NW>(wave, qb);
   const uint16_t* img = a.kvf + (size_t)ti.head * a.nb * TILE;
-  if (nt > 0) dma_tile<D, !SPARSE>(img + (size_t)ti.tile(0, SPARSE) * TILE, wave, lane, sKV);
+  if (nt > 0) dma_tile<D>(img + (size_t)ti.tile(0, SPARSE) * TILE, wave, lane, sKV);
   bf16x8 qf[QB][KS];
   load_q<D, QB, BQ, SPARSE>(a, ti.head, ti.qt, wave, lane, qf);
   f32x16 acc[QB][DB];
@@ -659,12 +654,23 @@ __device__ __forceinline__ void attn_kernel_body(const AttnArgs& a, uint16_t* sK
 #pragma unroll
     for (int db = 0; db < DB; ++db) acc[qb][db] = f32x16{};
   }
+  // Block-sparse: the list entries of the current and the next tile are carried in registers, and the
+  // entry two tiles ahead is loaded at the top of each iteration; only the tile barrier's vmcnt(0) waits
+  // for it, so no visit stalls on a list read before it can start the next copy and its own MFMAs.
+  int e_cur = 0, e_nxt = 0;
+  if constexpr (SPARSE) {
+    e_cur = nt > 0 ? ti.lst[0] : 0;
+    e_nxt = nt > 1 ? ti.lst[1] : 0;
+  }
   tile_barrier();
   for (int it = 0; it < nt; ++it) {
-    const int st = it & 1, tile = ti.tile(it, SPARSE);
+    int e_nn = 0;
+    if constexpr (SPARSE) e_nn = it + 2 < nt ? ti.lst[it + 2] : 0;
+    const int st = it & 1, tile = SPARSE ? (e_cur & 0xffffff) : it;
     if (it + 1 < nt)
-      dma_tile<D, !SPARSE>(img + (size_t)ti.tile(it + 1, SPARSE) * TILE, wave, lane, sKV + (st ^ 1) * TILE);
-    const int flags = ti.flags(it, SPARSE);
+      dma_tile<D>(img + (size_t)(SPARSE ? (e_nxt & 0xffffff) : it + 1) * TILE, wave, lane,
+                           sKV + (st ^ 1) * TILE);
+    const int flags = SPARSE ? (e_cur >> 24) : 0xff;
     int qm = 0;
 #pragma unroll
     for (int qb = 0; qb < QB; ++qb) qm |= ((flags >> rbit[qb]) & 1) << qb;
@@ -687,6 +693,8 @@ __device__ __forceinline__ void attn_kernel_body(const AttnArgs& a, uint16_t* sK
       for (int qb = 0; qb < QB; ++qb) pad[qb] += ((qm >> qb) & 1) ? max(0, (tile + 1) * BK - N) : 0;
     }
     tile_barrier();
+    e_cur = e_nxt;
+    e_nxt = e_nn;
   }
   if constexpr (MODE == kStatic) {
     // Padded keys sit in both lane halves; the row sum over both halves drops them exactly.
