@@ -12,6 +12,7 @@ from __future__ import annotations
 
 import argparse
 import hashlib
+import re
 import json
 import math
 import os
@@ -52,8 +53,12 @@ BLOCK_SRC = os.path.join(ROOT, "image_diffusion_transformer_amd", "csrc", "block
 
 
 def kernel_source_sha256(path: str = KERNEL_SRC) -> str:
-    with open(path, "rb") as f:
-        return hashlib.sha256(f.read()).hexdigest()
+    """SHA-256 of a kernel source's code: comments removed and whitespace runs collapsed, so that the stored
+    HBM-traffic figures stay valid across comment edits and lapse with any change to the code itself."""
+    with open(path, encoding="utf-8") as f:
+        text = f.read()
+    code = re.sub(r"//[^\n]*|/\*.*?\*/", " ", text, flags=re.S)
+    return hashlib.sha256(" ".join(code.split()).encode()).hexdigest()
 
 
 def log(msg):

@@ -23,7 +23,10 @@
 //    the channels each), RMS-normalised, rotated, scaled by log2(e)/sqrt(d) and
 //    kept in registers as bf16 MFMA B operands.
 //  * KV tiles are double-buffered in LDS: the next tile's fragment image is in
-//    flight (global->LDS, no registers) while the current one is consumed.
+//    flight (global->LDS, no registers, issued as inline assembly so that the
+//    fragment reads get graded LDS waits) while the current one is consumed.
+//    Block-sparse tiles take their KV tile and flags from a per-tile list whose
+//    entries are loaded two visits ahead.
 //  * S^T = K^ Q^T with v_mfma_f32_32x32x16_bf16 (keys on rows, queries on columns):
 //    each lane holds one query column, so the softmax row statistics need only
 //    in-lane reductions plus one permlane32 swap, and the S^T accumulator is
