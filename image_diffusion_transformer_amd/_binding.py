@@ -87,11 +87,52 @@ def _stream(stream):
     return ctypes.c_void_p(stream.cuda_stream)
 
 
+def _dev(t, name, dtype, shape=None):
+    """t as the C ABI reads it: a contiguous tensor of this dtype and shape (None: any size).  Where it lives
+    is checked by _on once every operand has passed this."""
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if t.dtype != dtype:
+        raise ValueError(f"{name} must be {dtype} (got {t.dtype})")
+    if shape is not None and (t.dim() != len(shape) or
+                              any(s is not None and int(a) != int(s) for a, s in zip(t.shape, shape))):
+        want = tuple("*" if s is None else s for s in shape)
+        raise ValueError(f"{name} must have shape {want} (got {tuple(t.shape)})")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    return t
+
+
+def _on(device, **tensors):
+    """Every operand in GPU memory, on one device: the library takes raw device pointers."""
+    for name, t in tensors.items():
+        if t is None:
+            continue
+        if t.device.type != "cuda":
+            raise ValueError(f"{name} must be in GPU memory (got {t.device})")
+        if t.device != device:
+            raise ValueError(f"{name} is on {t.device}, the other operands on {device}")
+
+
 def _shape(q, grid):
     T, H, W = (int(x) for x in grid)
-    if q.dim() != 3:
-        raise ValueError("q must be [N, heads, head_dim]")
+    _dev(q, "q", torch.bfloat16, (T * H * W, None, None))
     return T, H, W, int(q.shape[1]), int(q.shape[2])
+
+
+def _attn_operands(q, k, v, wq, wk, N, heads, d, nk=None):
+    """Checks q [N, heads, d], k and v [nk, heads, d] (v may be None) bf16 and wq, wk fp32 [d]."""
+    nk = N if nk is None else nk
+    _dev(q, "q", torch.bfloat16, (N, heads, d))
+    _dev(k, "k", torch.bfloat16, (nk, heads, d))
+    if v is not None:
+        _dev(v, "v", torch.bfloat16, (nk, heads, d))
+    _dev(wq, "wq", torch.float32, (d,))
+    _dev(wk, "wk", torch.float32, (d,))
+
+
+def _workspace(ws):
+    return _dev(ws, "workspace", torch.uint8, (None,))
 
 
 def dit_attn_workspace_bytes(T: int, H: int, W: int, heads: int, head_dim: int = HEAD_DIM, block: int = BLOCK) -> int:
@@ -114,10 +155,14 @@ def workspace_for(q, grid, device=None) -> torch.Tensor:
 def dit_attn_dense(q, k, v, wq, wk, grid, rope_theta=10000.0, eps=1e-6, o=None, workspace=None, stream=None):
     """O = attention(RoPE(RMSNorm(q)), RoPE(RMSNorm(k)), v); q, k, v bf16 [N, heads, 96] on the GPU."""
     T, H, W, heads, d = _shape(q, grid)
+    _attn_operands(q, k, v, wq, wk, T * H * W, heads, d)
     if o is None:
         o = torch.empty_like(q)
+    _dev(o, "o", torch.bfloat16, tuple(q.shape))
     if workspace is None:
         workspace = workspace_for(q, grid)
+    _workspace(workspace)
+    _on(q.device, q=q, k=k, v=v, wq=wq, wk=wk, o=o, workspace=workspace)
     _check(load_library().dit_attn_dense(_ptr(q), _ptr(k), _ptr(v), _ptr(wq), _ptr(wk), T, H, W, heads, d,
                                           rope_theta, eps, _ptr(o), _ptr(workspace), workspace.numel(),
                                           _stream(stream)))
@@ -128,11 +173,15 @@ def dit_attn_route(q, k, wq, wk, grid, sparsity, rope_theta=10000.0, eps=1e-6, b
                    workspace=None, stream=None):
     """Kept-block mask uint8 [heads, nb, nb] of the block router."""
     T, H, W, heads, d = _shape(q, grid)
+    _attn_operands(q, k, None, wq, wk, T * H * W, heads, d)
     nb = -(-(T * H * W) // block)
     if mask is None:
         mask = torch.empty((heads, nb, nb), dtype=torch.uint8, device=q.device)
+    _dev(mask, "mask", torch.uint8, (heads, nb, nb))
     if workspace is None:
         workspace = workspace_for(q, grid)
+    _workspace(workspace)
+    _on(q.device, q=q, k=k, wq=wq, wk=wk, mask=mask, workspace=workspace)
     _check(load_library().dit_attn_route(_ptr(q), _ptr(k), _ptr(wq), _ptr(wk), T, H, W, heads, d, rope_theta, eps,
                                           sparsity, block, _ptr(mask), _ptr(workspace), workspace.numel(),
                                           _stream(stream)))
@@ -143,10 +192,16 @@ def dit_attn_block_sparse(q, k, v, wq, wk, grid, mask, rope_theta=10000.0, eps=1
                           workspace=None, stream=None):
     """Attention restricted to the kept KV blocks of `mask` (uint8 [heads, nb, nb])."""
     T, H, W, heads, d = _shape(q, grid)
+    _attn_operands(q, k, v, wq, wk, T * H * W, heads, d)
+    nb = -(-(T * H * W) // block)
+    _dev(mask, "mask", torch.uint8, (heads, nb, nb))
     if o is None:
         o = torch.empty_like(q)
+    _dev(o, "o", torch.bfloat16, tuple(q.shape))
     if workspace is None:
         workspace = workspace_for(q, grid)
+    _workspace(workspace)
+    _on(q.device, q=q, k=k, v=v, wq=wq, wk=wk, mask=mask, o=o, workspace=workspace)
     _check(load_library().dit_attn_block_sparse(_ptr(q), _ptr(k), _ptr(v), _ptr(wq), _ptr(wk), T, H, W, heads, d,
                                                  rope_theta, eps, block, _ptr(mask), _ptr(o), _ptr(workspace),
                                                  workspace.numel(), _stream(stream)))
@@ -161,21 +216,23 @@ def dit_attn_joint(q, k, v, wq, wk, q_pos, k_pos, max_pos, rope_theta=10000.0, e
                    stream=None):
     """Joint attention: q bf16 [nq, heads, 96] at q_pos int32 [nq, 3], k / v bf16 [nk, heads, 96] at k_pos
     int32 [nk, 3] (t, h, w positions, each coordinate < max_pos); writes o [nq, heads, 96]."""
-    if q.dim() != 3 or k.dim() != 3:
-        raise ValueError("q and k must be [tokens, heads, head_dim]")
+    _dev(q, "q", torch.bfloat16, (None, None, None))
+    _dev(k, "k", torch.bfloat16, (None, None, None))
     nq, heads, d = (int(x) for x in q.shape)
     nk = int(k.shape[0])
-    if tuple(q_pos.shape) != (nq, 3) or tuple(k_pos.shape) != (nk, 3):
-        raise ValueError("q_pos must be [nq, 3] and k_pos [nk, 3]")
-    if q_pos.dtype != torch.int32 or k_pos.dtype != torch.int32:
-        raise ValueError("positions must be int32")
+    _attn_operands(q, k, v, wq, wk, nq, heads, d, nk)
+    _dev(q_pos, "q_pos", torch.int32, (nq, 3))
+    _dev(k_pos, "k_pos", torch.int32, (nk, 3))
     if o is None:
         o = torch.empty_like(q)
+    _dev(o, "o", torch.bfloat16, tuple(q.shape))
     if workspace is None:
         n = dit_attn_joint_workspace_bytes(nq, nk, heads, d, int(max_pos))
         if n == 0:
             raise DitAttnError(DIT_ERR_INVALID_ARG, "invalid sizes for joint workspace sizing")
         workspace = torch.empty(n, dtype=torch.uint8, device=q.device)
+    _workspace(workspace)
+    _on(q.device, q=q, k=k, v=v, wq=wq, wk=wk, q_pos=q_pos, k_pos=k_pos, o=o, workspace=workspace)
     _check(load_library().dit_attn_joint(_ptr(q), _ptr(k), _ptr(v), _ptr(wq), _ptr(wk), _ptr(q_pos), _ptr(k_pos),
                                           nq, nk, heads, d, int(max_pos), rope_theta, eps, _ptr(o), _ptr(workspace),
                                           workspace.numel(), _stream(stream)))
@@ -183,16 +240,23 @@ def dit_attn_joint(q, k, v, wq, wk, q_pos, k_pos, max_pos, rope_theta=10000.0, e
 
 
 def _rows(x, name):
-    if x.dim() != 2 or x.dtype != torch.bfloat16 or not x.is_contiguous():
-        raise ValueError(f"{name} must be a contiguous bf16 [tokens, width] tensor")
+    _dev(x, name, torch.bfloat16, (None, None))
     return int(x.shape[0]), int(x.shape[1])
+
+
+def _vec(t, name, hidden):
+    return _dev(t, name, torch.float32, (hidden,))
 
 
 def dit_adaln_modulate(x, shift, scale, eps=1e-6, h=None, stream=None):
     """AdaLN update: h = LayerNorm(x) * (1 + scale) + shift; x bf16 [tokens, hidden], shift / scale fp32 [hidden]."""
     tokens, hidden = _rows(x, "x")
+    _vec(shift, "shift", hidden)
+    _vec(scale, "scale", hidden)
     if h is None:
         h = torch.empty_like(x)
+    _dev(h, "h", torch.bfloat16, (tokens, hidden))
+    _on(x.device, x=x, shift=shift, scale=scale, h=h)
     _check(load_library().dit_adaln_modulate(_ptr(x), _ptr(shift), _ptr(scale), tokens, hidden, eps, _ptr(h),
                                              _stream(stream)))
     return h
@@ -202,12 +266,22 @@ def dit_gated_residual(x, y, gate, shift=None, scale=None, eps=1e-6, x_out=None,
     """x_out = x + gate * y and, if ``modulate``, h = LayerNorm(x_out) * (1 + scale) + shift from the float32 sum.
     Returns (x_out, h); h is None without modulation.  x_out may be x (in-place)."""
     tokens, hidden = _rows(x, "x")
+    _dev(y, "y", torch.bfloat16, (tokens, hidden))
+    _vec(gate, "gate", hidden)
+    if modulate:
+        _vec(shift, "shift", hidden)
+        _vec(scale, "scale", hidden)
     if x_out is None:
         x_out = torch.empty_like(x)
+    _dev(x_out, "x_out", torch.bfloat16, (tokens, hidden))
     if modulate and h is None:
         h = torch.empty_like(x)
     if not modulate:
         h = None
+    else:
+        _dev(h, "h", torch.bfloat16, (tokens, hidden))
+    _on(x.device, x=x, y=y, gate=gate, shift=shift if modulate else None, scale=scale if modulate else None,
+        x_out=x_out, h=h)
     _check(load_library().dit_gated_residual(_ptr(x), _ptr(y), _ptr(gate), _ptr(shift), _ptr(scale), tokens, hidden,
                                              eps, _ptr(x_out), _ptr(h), _stream(stream)))
     return x_out, h
@@ -216,9 +290,13 @@ def dit_gated_residual(x, y, gate, shift=None, scale=None, eps=1e-6, x_out=None,
 def dit_swiglu(gate_up, out=None, stream=None):
     """out = silu(g) * u for gate_up = [g | u], bf16 [tokens, 2 ffn] -> [tokens, ffn]."""
     tokens, width = _rows(gate_up, "gate_up")
+    if width % 2:
+        raise ValueError(f"gate_up must hold the gate and up halves: even width (got {width})")
     ffn = width // 2
     if out is None:
         out = torch.empty((tokens, ffn), dtype=gate_up.dtype, device=gate_up.device)
+    _dev(out, "out", torch.bfloat16, (tokens, ffn))
+    _on(gate_up.device, gate_up=gate_up, out=out)
     _check(load_library().dit_swiglu(_ptr(gate_up), tokens, ffn, _ptr(out), _stream(stream)))
     return out
 
