@@ -5,7 +5,7 @@ A step is one full layer: dense attention over the whole token grid for all head
 seeded synthetic bf16 tensors already resident in HBM when the timed region
 starts.  Prints ONE JSON line.
 
-    python bench.py [--steps K] [--warmup W] [--workload v5|image|v5s|v10s|v10d|v5h7|j_edit2|b_v5]
+    python bench.py [--steps K] [--warmup W] [--workload v5|image|v5s|v10s|v10d|v5h7|v5w|v5sw|j_edit2|b_v5]
                     [--no-cpu-baseline] [--calib-copy]
 """
 from __future__ import annotations
@@ -40,6 +40,10 @@ DESCR = {
     "v5d128": ("dense attention at head dim 128, 124,992 tokens, 42 heads x 128 (the same 5376 hidden width; "
                "RoPE chunks 44/42/42)"),
     "v5s128": ("route + block-sparse attention (sparsity 0.75) at head dim 128, 124,992 tokens, 42 heads x 128"),
+    "v5w": ("dense attention, 124,992 tokens, 56 heads x 96, norm weights 1.75(1+0.1N(0,1)): logits past the "
+            "static-shift bound, so the running-maximum softmax runs"),
+    "v5sw": ("route + block-sparse attention (sparsity 0.75), 124,992 tokens, 56 heads x 96, norm weights "
+             "1.75(1+0.1N(0,1)) (running-maximum softmax)"),
     "s4": "dense attention, small grid 5x24x40 = 4,800 tokens, 2 heads x 96 (contract checks)",
     "b_mid": "operators around attention on 1,000 tokens, hidden 5376, FFN 14336 (contract checks)",
     "b_v5": ("operators around attention at 124,992 tokens, hidden 5376, FFN 14336: AdaLN update, gated "
@@ -59,6 +63,16 @@ def kernel_source_sha256(path: str = KERNEL_SRC) -> str:
         text = f.read()
     code = re.sub(r"//[^\n]*|/\*.*?\*/", " ", text, flags=re.S)
     return hashlib.sha256(" ".join(code.split()).encode()).hexdigest()
+
+
+def softmax_mode(wq: np.ndarray, wk: np.ndarray, d: int) -> str:
+    """Which attention kernel does the work for these norm weights: "static" (exp2 of the logits with no
+    shift) when log2(e) sqrt(d) max_i u_i v_i, times a 2% margin, is at most 48 -- u_i, v_i being the larger
+    |weight| of channel pair i in w_q, w_k -- else "online" (running maximum).  Used to name the kernel."""
+    u = np.maximum(np.abs(wq[0::2]), np.abs(wq[1::2])).astype(np.float64)
+    v = np.maximum(np.abs(wk[0::2]), np.abs(wk[1::2])).astype(np.float64)
+    bound = math.log2(math.e) * math.sqrt(d) * float(np.max(u * v)) * 1.02
+    return "static" if bound <= 48.0 else "online"
 
 
 def log(msg):
@@ -346,14 +360,15 @@ def main():
         "scaling": "weak",
         "vs_baseline": None,
         "dtype": "bf16",
-        "data": "synthetic (seeded N(0,1) bf16 Q/K/V, video grids plus smooth sinusoid component; norm weights 1+0.1N(0,1))",
+        "data": ("synthetic (seeded N(0,1) bf16 Q/K/V, video grids plus smooth sinusoid component; norm weights "
+                 + ("1+0.1N(0,1))" if wl.weight_scale == 1.0 else f"{wl.weight_scale:g}(1+0.1N(0,1)))")),
         "config": {"workload": f"{wl.name}: {DESCR[wl.name]}", "tokens": N, "heads": H, "head_dim": d,
                    "grid": [wl.T, wl.H, wl.W], "mode": wl.mode, "sparsity": wl.sparsity if sparse else None},
         "ms_per_layer": round(ms_step, 3),
         "frac_of_bf16_peak": round(tflops / PEAK_BF16_TFLOPS, 4),
         "roofline": {"bound": "mfma", "achieved": round(attn_tflops, 2), "peak": PEAK_BF16_TFLOPS,
                      "unit": "TFLOP/s", "frac": round(attn_tflops / PEAK_BF16_TFLOPS, 4), "traffic": traffic,
-                     "kernel": f"attn_static_kernel<{d}, " + ("true>" if sparse else "false>"),
+                     "kernel": f"attn_{softmax_mode(x.wq, x.wk, d)}_kernel<{d}, " + ("true>" if sparse else "false>"),
                      "timed": "whole call: K^/V fragment prepass + attention kernels",
                      "kernel_ms": round(ms_attn, 3), "flops_per_launch": flops},
     }

@@ -13,7 +13,8 @@ report's test setup):
 * video grids add a smooth, position-dependent component so the block router
   has structure to find: three random low-frequency sinusoids over (t, h, w),
   each with amplitude 0.5 and a random sign per (tensor, head, channel).
-* RMSNorm weights: 1 + 0.1 * N(0, 1), float32, one vector of 96 per Q and K.
+* RMSNorm weights: 1 + 0.1 * N(0, 1), float32, one vector of 96 per Q and K (1.75 times that for
+  the workloads that exercise the running-maximum softmax).
 
 Generation is chunked over tokens; every chunk draws from its own
 ``SeedSequence([seed, tensor, chunk])`` stream, so results do not depend on
@@ -48,6 +49,7 @@ class Workload:
     eps: float = 1e-6
     fp32_inputs: bool = False    # the tiny grid also keeps its float32 draw
     head_dim: int = HEAD_DIM     # 96 (the model's); 128 for the head-dim-128 instantiation
+    weight_scale: float = 1.0    # RMSNorm weights are weight_scale * (1 + 0.1 N(0, 1))
     notes: str = field(default="", compare=False)
 
     @property
@@ -90,6 +92,12 @@ WORKLOADS = {
                  notes="5 s video grid, 42 heads x 128 (hidden 5376), dense"),
         Workload("v5s128", 31, 48, 84, 42, seed=34, smooth=True, head_dim=128, mode="sparse", sparsity=0.75,
                  notes="same tensors as v5d128, block-sparse at sparsity 0.75"),
+        # norm weights 1.75 times as large: the logit bound (59.6 in base 2) is past what exp2 takes without
+        # a shift, so the kernels keep a running maximum (the general softmax path)
+        Workload("v5w", 31, 48, 84, 56, seed=2, smooth=True, weight_scale=1.75,
+                 notes="same tensors as v5, norm weights 1.75(1 + 0.1 N(0,1)), dense"),
+        Workload("v5sw", 31, 48, 84, 56, seed=2, smooth=True, weight_scale=1.75, mode="sparse", sparsity=0.75,
+                 notes="same tensors as v5, norm weights 1.75(1 + 0.1 N(0,1)), block-sparse at sparsity 0.75"),
     ]
 }
 
@@ -152,11 +160,18 @@ def _smooth_params(seed: int, heads: int, d: int = HEAD_DIM):
     return np.array(freqs, dtype=np.float64), np.array(phases), signs
 
 
-def _weights(seed: int, d: int = HEAD_DIM):
+def _weights(seed: int, d: int = HEAD_DIM, scale: float = 1.0):
     g = np.random.Generator(np.random.PCG64(np.random.SeedSequence([seed, 7])))
-    wq = (1.0 + 0.1 * g.standard_normal(d)).astype(np.float32)
-    wk = (1.0 + 0.1 * g.standard_normal(d)).astype(np.float32)
+    wq = (scale * (1.0 + 0.1 * g.standard_normal(d))).astype(np.float32)
+    wk = (scale * (1.0 + 0.1 * g.standard_normal(d))).astype(np.float32)
     return wq, wk
+
+
+def norm_weights(wl: Workload | str) -> tuple[np.ndarray, np.ndarray]:
+    """The workload's RMSNorm weights (w_q, w_k), float32 [head_dim] each, without drawing Q/K/V."""
+    if isinstance(wl, str):
+        wl = WORKLOADS[wl]
+    return _weights(wl.seed, wl.head_dim, wl.weight_scale)
 
 
 def _fill_chunk(wl: Workload, tensor: int, chunk: int, smooth, out_bits, out_f32):
@@ -201,7 +216,7 @@ def make_inputs(wl: Workload | str, threads: int | None = None) -> Inputs:
     else:
         with ThreadPoolExecutor(threads) as ex:
             list(ex.map(lambda tc: _fill_chunk(wl, tc[0], tc[1], smooth, bits[tc[0]], f32[tc[0]]), jobs))
-    wq, wk = _weights(wl.seed, d)
+    wq, wk = norm_weights(wl)
     return Inputs(wl, BF16Tensor(bits[0]), BF16Tensor(bits[1]), BF16Tensor(bits[2]), wq, wk,
                   *f32)
 

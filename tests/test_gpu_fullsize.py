@@ -8,7 +8,7 @@ import torch
 import image_diffusion_transformer_amd as dit
 from oracle import attention as A
 from oracle import router as R
-from synth import WORKLOADS, make_inputs
+from synth import WORKLOADS, make_inputs, norm_weights
 
 pytestmark = pytest.mark.gpu
 DEV = torch.device("cuda:0")
@@ -103,3 +103,38 @@ def test_route_and_sparse_full_size_v10():
     ref = A.attention(x.q, x.k, x.v, x.wq, x.wk, wl.T, wl.H, wl.W, wl.theta, wl.eps, heads=heads, rows=rows,
                       mask=full_mask)
     check(got, ref, f"sparse v10s blocks {blocks}")
+
+
+def test_running_max_full_size_v5w(v5):
+    """The same 5 s video tensors with norm weights 1.75(1 + 0.1 N(0,1)), whose logit bound is past the
+    static shift: dense and route + block-sparse attention run the running-maximum kernels, at full size."""
+    x, (q, k, v, _, _) = v5
+    wl = WORKLOADS["v5w"]
+    wq_np, wk_np = norm_weights(wl)
+    wq, wk = torch.from_numpy(wq_np).to(DEV), torch.from_numpy(wk_np).to(DEV)
+    g = (wl.T, wl.H, wl.W)
+    print("case dense full v5w", flush=True)
+    o = dit.dit_attn_dense(q, k, v, wq, wk, g, wl.theta, wl.eps)
+    torch.cuda.synchronize()
+    blocks, rows = sample_rows(wl.nb, wl.N, seed=77)
+    heads = [3, 41]
+    got = o[torch.from_numpy(rows).to(DEV)][:, heads].float().cpu().numpy()
+    ref = A.attention(x.q, x.k, x.v, wq_np, wk_np, wl.T, wl.H, wl.W, wl.theta, wl.eps, heads=heads, rows=rows)
+    check(got, ref, f"dense v5w blocks {blocks}")
+
+    sw = WORKLOADS["v5sw"]
+    print("case route+sparse full v5sw", flush=True)
+    ws = dit.workspace_for(q, g)
+    mask = dit.dit_attn_route(q, k, wq, wk, g, sw.sparsity, sw.theta, sw.eps, workspace=ws)
+    o = dit.dit_attn_block_sparse(q, k, v, wq, wk, g, mask, sw.theta, sw.eps, o=o, workspace=ws)
+    torch.cuda.synchronize()
+    m_gpu = mask.cpu().numpy()
+    m_ref = R.route_mask(x.q, x.k, wq_np, wk_np, sw.T, sw.H, sw.W, sw.sparsity, sw.theta, sw.eps, heads=heads)
+    for i, hd in enumerate(heads):
+        assert np.array_equal(m_gpu[hd], m_ref[i]), f"head {hd}: router rows differ"
+    got = o[torch.from_numpy(rows).to(DEV)][:, heads].float().cpu().numpy()
+    full_mask = np.zeros_like(m_gpu)
+    full_mask[heads] = m_ref
+    ref = A.attention(x.q, x.k, x.v, wq_np, wk_np, sw.T, sw.H, sw.W, sw.theta, sw.eps, heads=heads, rows=rows,
+                      mask=full_mask)
+    check(got, ref, f"sparse v5sw blocks {blocks}")

@@ -60,3 +60,26 @@ def test_bound_is_reached_by_an_input_on_the_best_pair():
     b = pair_bound(wq, wk)
     assert np.isclose(np.diag(L).min(), b, rtol=1e-12)
     assert np.abs(L).max() <= b * (1 + 1e-12)
+
+
+def test_bench_names_the_kernel_the_weights_select():
+    """bench.py labels its roofline with the kernel the weights select: the 1 + 0.1 N(0,1) weights stay
+    under the bound, the 1.75 times larger ones of the running-maximum workloads do not; equal weights c give the
+    bound log2(e) sqrt(d) c^2 (times the 2% margin), which decides on either side of 48."""
+    import importlib.util
+    import os
+
+    from synth import WORKLOADS, norm_weights
+    root = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+    spec = importlib.util.spec_from_file_location("bench_under_test", os.path.join(root, "bench.py"))
+    bench = importlib.util.module_from_spec(spec)
+    spec.loader.exec_module(bench)
+    for name, want in (("v5", "static"), ("v5s", "static"), ("v5d128", "static"), ("v5w", "online"),
+                       ("v5sw", "online")):
+        wq, wk = norm_weights(name)
+        assert bench.softmax_mode(wq, wk, WORKLOADS[name].head_dim) == want, name
+    for d in (96, 128):
+        c_edge = np.sqrt(48.0 / (np.log2(np.e) * np.sqrt(d) * 1.02))
+        for f, want in ((0.999, "static"), (1.001, "online")):
+            w = np.full(d, c_edge * f, dtype=np.float32)
+            assert bench.softmax_mode(w, w, d) == want
