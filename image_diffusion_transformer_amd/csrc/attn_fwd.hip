@@ -646,6 +646,12 @@ __device__ __forceinline__ void attn_kernel_body(const AttnArgs& a, uint16_t* sK
   if (nt > 0) dma_tile<D>(img + (size_t)ti.tile(0, SPARSE) * TILE, wave, lane, sKV);
   bf16x8 qf[QB][KS];
   load_q<D, QB, BQ, SPARSE>(a, ti.head, ti.qt, wave, lane, qf);
+  // Finish Q here: left free, the compiler sinks the norm and rotation below the first tile barrier,
+  // next to the loop, and carries the raw loads across it in scratch.
+#pragma unroll
+  for (int qb = 0; qb < QB; ++qb)
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) asm volatile("" ::"v"(qf[qb][ks]));
   f32x16 acc[QB][DB];
   float m[QB], l[QB];
   int pad[QB];                                     // static mode: keys past the grid counted in l
