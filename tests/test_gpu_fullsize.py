@@ -82,7 +82,7 @@ def test_route_and_sparse_full_size_v5(v5):
     check(got, ref, f"sparse v5s blocks {blocks}")
 
 
-def test_route_and_sparse_full_size_v10():
+def test_route_sparse_and_dense_full_size_v10():
     wl = WORKLOADS["v10s"]
     x = make_inputs(wl)
     q, k, v, wq, wk = upload(x)
@@ -103,6 +103,13 @@ def test_route_and_sparse_full_size_v10():
     ref = A.attention(x.q, x.k, x.v, x.wq, x.wk, wl.T, wl.H, wl.W, wl.theta, wl.eps, heads=heads, rows=rows,
                       mask=full_mask)
     check(got, ref, f"sparse v10s blocks {blocks}")
+    # the dense layer on the same tensors (the 10 s dense-equivalent comparison)
+    print("case dense full v10d", flush=True)
+    o = dit.dit_attn_dense(q, k, v, wq, wk, g, wl.theta, wl.eps, o=o, workspace=ws)
+    torch.cuda.synchronize()
+    got = o[torch.from_numpy(rows).to(DEV)][:, heads].float().cpu().numpy()
+    ref = A.attention(x.q, x.k, x.v, x.wq, x.wk, wl.T, wl.H, wl.W, wl.theta, wl.eps, heads=heads, rows=rows)
+    check(got, ref, f"dense v10d blocks {blocks}")
 
 
 def test_running_max_full_size_v5w(v5):
