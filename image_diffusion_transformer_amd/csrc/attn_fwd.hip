@@ -61,7 +61,7 @@ typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 
 constexpr int BK = kBlock;    // keys per KV tile (= router block)
-constexpr float kTau = 8.0f;  // lazy-rescale threshold, base-2 log units
+constexpr float kSumLimit = 256.0f;  // 2^8: largest per-lane block sum of p before the running max moves
 
 // Fragment image of one (head, 128-key tile), written by kv_prep_kernel: FRAGS fragments of 512 bf16
 // (lane l owns elements 8l..8l+7).  With KS = d/16 channel steps and DB = d/32 channel blocks:
@@ -373,22 +373,32 @@ __device__ __forceinline__ void softmax_online(f32x16 (&S)[QB], bool ragged, int
 #pragma unroll
   for (int qb = 0; qb < QB; ++qb) {
     if (((QM >> qb) & 1) == 0) continue;
-    float mx = S[qb][0];
+    // p = exp2(S - m) with the current running max.  Every p is at most its lane's block sum, so while
+    // every sum stays within kSumLimit no p exceeds it and m needs no update: the block max is only
+    // computed when some sum of the wave is larger, infinite or NaN (the first block, where m is still
+    // the -1e30 start, always is).  Then m moves to the block max, O and l are rescaled and p is redone.
+    float p[16];
 #pragma unroll
-    for (int i = 1; i < 16; ++i) mx = fmaxf(mx, S[qb][i]);
-    mx = pair_max(mx);
-    if (__builtin_amdgcn_ballot_w64(mx > m[qb] + kTau)) {
+    for (int i = 0; i < 16; ++i) p[i] = __builtin_amdgcn_exp2f(S[qb][i] - m[qb]);
+    float lb = 0.f;
+    pack_probs(p, lb, P[qb]);
+    if (__builtin_amdgcn_ballot_w64(!(lb <= kSumLimit))) {
+      float mx = S[qb][0];
+#pragma unroll
+      for (int i = 1; i < 16; ++i) mx = fmaxf(mx, S[qb][i]);
+      mx = pair_max(mx);
       const float mn = fmaxf(m[qb], mx);
       const float alpha = __builtin_amdgcn_exp2f(m[qb] - mn);
       l[qb] *= alpha;
 #pragma unroll
       for (int db = 0; db < DB; ++db) acc[qb][db] *= alpha;
       m[qb] = mn;
-    }
-    float p[16];
 #pragma unroll
-    for (int i = 0; i < 16; ++i) p[i] = __builtin_amdgcn_exp2f(S[qb][i] - m[qb]);
-    pack_probs(p, l[qb], P[qb]);
+      for (int i = 0; i < 16; ++i) p[i] = __builtin_amdgcn_exp2f(S[qb][i] - m[qb]);
+      lb = 0.f;
+      pack_probs(p, lb, P[qb]);
+    }
+    l[qb] += lb;
   }
 }
 
