@@ -34,10 +34,10 @@
 //  * O^T += V^T P^T with the same MFMA, V^T fragments read from LDS with one
 //    16-byte load per lane.
 //  * Static-shift softmax when the QK-RMSNorm logit bound allows it (p = exp2(S),
-//    no running max); otherwise an online softmax in base 2 with a lazy rescale:
-//    the running max only moves (and O, l are rescaled) when a block max exceeds
-//    it by more than 8, so exp2 arguments stay <= 8; the final O / l is exact for
-//    any stale max.
+//    no running max); otherwise an online softmax in base 2 whose running max
+//    only moves (and O, l are rescaled) when a lane's block sum of p passes 2^8,
+//    so every p stays <= 2^8 and the block max is computed only then; the final
+//    O / l is exact for any stale max.
 //  * Row sums accumulate the bf16-rounded probabilities (v_dot2_f32_bf16), the
 //    same values the PV product uses.
 #include "dit_internal.h"

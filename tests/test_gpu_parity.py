@@ -121,8 +121,8 @@ def static_shift_bound(wq, wk, d=96):
 def test_dense_running_max_rescale(big_weight):
     """Queries 0..63 meet keys aligned with them (logit ~ sqrt(96) ~ 9.4) only in the second tile,
     well above every earlier block max (~3).  With one large query weight (channel pair 0) the logit
-    bound exceeds the static-shift limit, the running-max kernel runs, and its max must move by more
-    than the lazy threshold there, rescaling O and the row sum.  With standard weights the static
+    bound exceeds the static-shift limit, the running-max kernel runs, and the block sums of p pass 2^8
+    there, so its max must move, rescaling O and the row sum.  With standard weights the static
     kernel runs the same case."""
     wl = custom_workload(1, 5, 40, 2, seed=41, smooth=False)        # N = 200: keys 136..199 aligned
     x = make_inputs(wl)
