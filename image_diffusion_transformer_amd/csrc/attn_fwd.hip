@@ -356,20 +356,24 @@ __device__ __forceinline__ bool key_live(int key0, int i, int half, int N) {
   return key0 + 8 * (i >> 2) + 4 * half + (i & 3) < N;
 }
 
+// Logits of keys past the grid (key index >= N, in the last, ragged tile) set to -inf: p = 0 there.
+template <int QB>
+__device__ __forceinline__ void mask_past_grid(f32x16 (&S)[QB], int key0, int N, int lane) {
+  const int half = lane >> 5;
+#pragma unroll
+  for (int i = 0; i < 16; ++i) {
+    const bool live = key_live(key0, i, half, N);
+#pragma unroll
+    for (int qb = 0; qb < QB; ++qb) S[qb][i] = live ? S[qb][i] : -INFINITY;
+  }
+}
+
 // Online (running-max) softmax of one sub-block; keys >= N get probability 0.
 template <int DB, int QB, int QM = (1 << QB) - 1>
 __device__ __forceinline__ void softmax_online(f32x16 (&S)[QB], bool ragged, int key0, int N, int lane,
                                                float (&m)[QB], float (&l)[QB], f32x16 (&acc)[QB][DB],
                                                bf16x8 (&P)[QB][2]) {
-  const int half = lane >> 5;
-  if (ragged) {
-#pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      const bool live = key_live(key0, i, half, N);
-#pragma unroll
-      for (int qb = 0; qb < QB; ++qb) S[qb][i] = live ? S[qb][i] : -INFINITY;
-    }
-  }
+  if (ragged) mask_past_grid<QB>(S, key0, N, lane);
 #pragma unroll
   for (int qb = 0; qb < QB; ++qb) {
     if (((QM >> qb) & 1) == 0) continue;
@@ -402,8 +406,7 @@ __device__ __forceinline__ void softmax_online(f32x16 (&S)[QB], bool ragged, int
   }
 }
 
-// Static-shift softmax of one sub-block: p = exp2(S).  Keys past the grid (zero K^ and V) give S = 0 and
-// p = 1; they add nothing to O and the kernel takes their count off the row sum at the end.
+// Static-shift softmax of one sub-block: p = exp2(S).  The caller has masked keys past the grid to -inf.
 template <int QB, int QM = (1 << QB) - 1>
 __device__ __forceinline__ void softmax_static(const f32x16 (&S)[QB], float (&l)[QB], bf16x8 (&P)[QB][2]) {
 #pragma unroll
@@ -619,6 +622,9 @@ __device__ __forceinline__ void tile_body(const uint16_t* T_, int lane, const bf
       kp[0] = *(const bf16x8*)(T_ + (nk * KS + 0) * kFrag + lane * 8);
       kp[1] = *(const bf16x8*)(T_ + (nk * KS + 1) * kFrag + lane * 8);
       __builtin_amdgcn_sched_barrier(0);
+      // Keys past the grid are masked, not counted and taken off the row sum at the end: when every real
+      // logit of a row is very negative, its sum would vanish next to that count in fp32.
+      if (ragged) mask_past_grid<QB>(S, key0 + kb * 32, N, lane);
       bf16x8 P[QB][2];
       softmax_static<QB, QM>(S, l, P);
       pv_block<D, QB, QM>(T_, kb, lane, P, acc);
@@ -636,9 +642,7 @@ __device__ __forceinline__ void tile_body(const uint16_t* T_, int lane, const bf
   }
 }
 
-// Static mode: keys past the grid have zero K^ and V: S = 0 and p = 1 there, they add nothing to O and
-// their count is taken off the row sum at the end -- no masking inside the loop.  Online mode (for norm
-// weights whose logit bound is too large for the static shift) masks them.
+// Both modes mask keys past the grid (zero K^ and V) in the last, ragged KV tile only.
 template <int D, bool SPARSE, int MODE>
 __device__ __forceinline__ void attn_kernel_body(const AttnArgs& a, uint16_t* sKV) {
   constexpr int QB = Head<D>::QB, BQ = Head<D>::BQ, TILE = Head<D>::TILE;
@@ -664,12 +668,10 @@ __device__ __forceinline__ void attn_kernel_body(const AttnArgs& a, uint16_t* sK
     for (int ks = 0; ks < KS; ++ks) asm volatile("" ::"v"(qf[qb][ks]));
   f32x16 acc[QB][DB];
   float m[QB], l[QB];
-  int pad[QB];                                     // static mode: keys past the grid counted in l
 #pragma unroll
   for (int qb = 0; qb < QB; ++qb) {
     m[qb] = -1e30f;
     l[qb] = 0.f;
-    pad[qb] = 0;
 #pragma unroll
     for (int db = 0; db < DB; ++db) acc[qb][db] = f32x16{};
   }
@@ -707,18 +709,9 @@ __device__ __forceinline__ void attn_kernel_body(const AttnArgs& a, uint16_t* sK
     } else {
       tile_body<D, QB, (1 << QB) - 1, MODE>(T_, lane, qf, acc, m, l, ragged, tile * BK, N);
     }
-    if constexpr (MODE == kStatic) {
-#pragma unroll
-      for (int qb = 0; qb < QB; ++qb) pad[qb] += ((qm >> qb) & 1) ? max(0, (tile + 1) * BK - N) : 0;
-    }
     tile_barrier();
     e_cur = e_nxt;
     e_nxt = e_nn;
-  }
-  if constexpr (MODE == kStatic) {
-    // Padded keys sit in both lane halves; the row sum over both halves drops them exactly.
-#pragma unroll
-    for (int qb = 0; qb < QB; ++qb) l[qb] -= (lane < 32) ? (float)pad[qb] : 0.f;
   }
   store_o<D, QB, BQ, SPARSE>(a, ti.head, ti.qt, wave, lane, acc, l);
 }

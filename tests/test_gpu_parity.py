@@ -251,3 +251,41 @@ def test_route_then_sparse_pipeline():
     np.testing.assert_array_equal(m.cpu().numpy(), mask)
     ref = A.attention(x.q, x.k, x.v, x.wq, x.wk, wl.T, wl.H, wl.W, mask=mask)
     check_close(as_np(o), ref, "route+sparse")
+
+
+@pytest.mark.parametrize("sparse", [False, True])
+def test_static_rows_whose_logits_are_all_very_negative(sparse):
+    """Every key anti-aligned with every query, with logits about -46 in base 2, on a ragged grid
+    (500 tokens, so the last KV tile has 12 keys past the grid), under weights that still select the
+    static-shift kernel.  The row sums are then about 500 * 2^-46.  Keys past the grid must be masked out.
+    If they were counted with p = 1 and their count subtracted at the end, the row sum would vanish
+    next to that count in fp32 and O would drop to zero.  q and k put all their energy on the
+    lowest-frequency RoPE pair of each axis, whose rotation over the grid is below 0.01 rad."""
+    T, H, W, d = 1, 10, 50, 96
+    N = T * H * W
+    c = np.sqrt(47.0 / (np.log2(np.e) * np.sqrt(d) * 1.02))
+    w = np.full(d, c, dtype=np.float32)
+    assert 46.5 < static_shift_bound(w, w) <= 48
+    x = np.zeros((N, 1, d), dtype=np.float32)
+    x[:, 0, [30, 62, 94]] = 1.0
+    rng = np.random.default_rng(11)
+    v = rng.standard_normal((N, 1, d)).astype(np.float32)
+    qb, kb, vb = f32_to_bf16_bits(x), f32_to_bf16_bits(-x), f32_to_bf16_bits(v)
+
+    def t(bits):
+        return torch.from_numpy(bits.view(np.int16)).to(DEV).view(torch.bfloat16)
+
+    wt = torch.from_numpy(w).to(DEV)
+    if sparse:
+        nb = -(-N // 128)
+        mask = np.ones((1, nb, nb), dtype=np.uint8)
+        o = dit.dit_attn_block_sparse(t(qb), t(kb), t(vb), wt, wt, (T, H, W), torch.from_numpy(mask).to(DEV))
+    else:
+        o = dit.dit_attn_dense(t(qb), t(kb), t(vb), wt, wt, (T, H, W))
+    torch.cuda.synchronize()
+    f = lambda b: (b.astype(np.uint32) << 16).view(np.float32)
+    L = A.logits(f(qb), f(kb), w, w, T, H, W, 0)
+    assert L.max() * np.log2(np.e) < -45                      # every logit far below zero
+    ref = A.attention(f(qb), f(kb), f(vb), w, w, T, H, W)
+    assert np.abs(ref[:, 0] - f(vb)[:, 0].mean(axis=0)).max() < 0.05   # nearly uniform weights
+    check_close(as_np(o), ref, f"all logits very negative, {'sparse' if sparse else 'dense'}")
