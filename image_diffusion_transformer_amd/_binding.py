@@ -7,6 +7,7 @@ been built (there is no fallback).
 """
 from __future__ import annotations
 
+import contextlib
 import ctypes
 import os
 import threading
@@ -17,13 +18,13 @@ LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libditattn.
 HEAD_DIM = 96
 BLOCK = 128
 
-DIT_OK, DIT_ERR_INVALID_ARG, DIT_ERR_UNSUPPORTED, DIT_ERR_WORKSPACE, DIT_ERR_HIP = range(5)
+DIT_OK, DIT_ERR_INVALID_ARG, DIT_ERR_UNSUPPORTED, DIT_ERR_WORKSPACE, DIT_ERR_HIP, DIT_ERR_HOST = range(6)
 STATUS_NAMES = {0: "DIT_OK", 1: "DIT_ERR_INVALID_ARG", 2: "DIT_ERR_UNSUPPORTED",
-                3: "DIT_ERR_WORKSPACE", 4: "DIT_ERR_HIP"}
+                3: "DIT_ERR_WORKSPACE", 4: "DIT_ERR_HIP", 5: "DIT_ERR_HOST"}
 
 EXPORTS = ("dit_attn_workspace_bytes", "dit_attn_keep_count", "dit_attn_dense", "dit_attn_route",
-           "dit_attn_block_sparse", "dit_attn_joint_workspace_bytes", "dit_attn_joint", "dit_attn_last_error",
-           "dit_adaln_modulate", "dit_gated_residual", "dit_swiglu")
+           "dit_attn_block_sparse", "dit_attn_joint_workspace_bytes", "dit_attn_joint", "dit_attn_set_launch_order",
+           "dit_attn_last_error", "dit_adaln_modulate", "dit_gated_residual", "dit_swiglu")
 
 _lib = None
 _lock = threading.Lock()
@@ -45,7 +46,7 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
             raise RuntimeError(f"{path} is not built; run image_diffusion_transformer_amd.build.build() first")
         lib = ctypes.CDLL(path)
         vp, i, f, sz = ctypes.c_void_p, ctypes.c_int, ctypes.c_float, ctypes.c_size_t
-        lib.dit_attn_workspace_bytes.argtypes = [i, i, i, i, i, i]
+        lib.dit_attn_workspace_bytes.argtypes = [i, i, i, i, i, i, f]
         lib.dit_attn_workspace_bytes.restype = sz
         lib.dit_attn_keep_count.argtypes = [i, f]
         lib.dit_attn_keep_count.restype = i
@@ -66,6 +67,8 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
         lib.dit_gated_residual.restype = i
         lib.dit_swiglu.argtypes = [vp, ll, i, vp, vp]
         lib.dit_swiglu.restype = i
+        lib.dit_attn_set_launch_order.argtypes = [i]
+        lib.dit_attn_set_launch_order.restype = i
         lib.dit_attn_last_error.argtypes = []
         lib.dit_attn_last_error.restype = ctypes.c_char_p
         _lib = lib
@@ -85,6 +88,14 @@ def _stream(stream):
     if stream is None:
         stream = torch.cuda.current_stream()
     return ctypes.c_void_p(stream.cuda_stream)
+
+
+def _on_stream(stream):
+    """Context in which a call allocates its temporaries (workspace, o, mask): on the stream the call runs on.
+    torch's caching allocator then hands that memory to other work on that stream only, which runs after the
+    call's kernels; allocated on another stream, a temporary freed at return could be reused while the
+    kernels still read or write it."""
+    return contextlib.nullcontext() if stream is None else torch.cuda.stream(stream)
 
 
 def _dev(t, name, dtype, shape=None):
@@ -135,20 +146,21 @@ def _workspace(ws):
     return _dev(ws, "workspace", torch.uint8, (None,))
 
 
-def dit_attn_workspace_bytes(T: int, H: int, W: int, heads: int, head_dim: int = HEAD_DIM, block: int = BLOCK) -> int:
-    return int(load_library().dit_attn_workspace_bytes(T, H, W, heads, head_dim, block))
+def dit_attn_workspace_bytes(T: int, H: int, W: int, heads: int, head_dim: int = HEAD_DIM, block: int = BLOCK,
+                             sparsity: float = 0.0) -> int:
+    return int(load_library().dit_attn_workspace_bytes(T, H, W, heads, head_dim, block, sparsity))
 
 
 def dit_attn_keep_count(nb: int, sparsity: float) -> int:
     return int(load_library().dit_attn_keep_count(nb, sparsity))
 
 
-def workspace_for(q, grid, device=None) -> torch.Tensor:
-    """Allocate a workspace tensor large enough for every entry point at this shape."""
+def workspace_for(q, grid, device=None, sparsity: float = 0.0) -> torch.Tensor:
+    """Allocate a workspace tensor large enough for every entry point at this shape (on the current stream)."""
     T, H, W, heads, d = _shape(q, grid)
-    n = dit_attn_workspace_bytes(T, H, W, heads, d, BLOCK)
+    n = dit_attn_workspace_bytes(T, H, W, heads, d, BLOCK, sparsity)
     if n == 0:
-        raise DitAttnError(DIT_ERR_INVALID_ARG, "invalid shape for workspace sizing")
+        raise DitAttnError(DIT_ERR_INVALID_ARG, "invalid shape or sparsity for workspace sizing")
     return torch.empty(n, dtype=torch.uint8, device=device or q.device)
 
 
@@ -156,11 +168,12 @@ def dit_attn_dense(q, k, v, wq, wk, grid, rope_theta=10000.0, eps=1e-6, o=None, 
     """O = attention(RoPE(RMSNorm(q)), RoPE(RMSNorm(k)), v); q, k, v bf16 [N, heads, 96] on the GPU."""
     T, H, W, heads, d = _shape(q, grid)
     _attn_operands(q, k, v, wq, wk, T * H * W, heads, d)
-    if o is None:
-        o = torch.empty_like(q)
+    with _on_stream(stream):
+        if o is None:
+            o = torch.empty_like(q)
+        if workspace is None:
+            workspace = workspace_for(q, grid)
     _dev(o, "o", torch.bfloat16, tuple(q.shape))
-    if workspace is None:
-        workspace = workspace_for(q, grid)
     _workspace(workspace)
     _on(q.device, q=q, k=k, v=v, wq=wq, wk=wk, o=o, workspace=workspace)
     _check(load_library().dit_attn_dense(_ptr(q), _ptr(k), _ptr(v), _ptr(wq), _ptr(wk), T, H, W, heads, d,
@@ -175,11 +188,12 @@ def dit_attn_route(q, k, wq, wk, grid, sparsity, rope_theta=10000.0, eps=1e-6, b
     T, H, W, heads, d = _shape(q, grid)
     _attn_operands(q, k, None, wq, wk, T * H * W, heads, d)
     nb = -(-(T * H * W) // block)
-    if mask is None:
-        mask = torch.empty((heads, nb, nb), dtype=torch.uint8, device=q.device)
+    with _on_stream(stream):
+        if mask is None:
+            mask = torch.empty((heads, nb, nb), dtype=torch.uint8, device=q.device)
+        if workspace is None:
+            workspace = workspace_for(q, grid, sparsity=sparsity)
     _dev(mask, "mask", torch.uint8, (heads, nb, nb))
-    if workspace is None:
-        workspace = workspace_for(q, grid)
     _workspace(workspace)
     _on(q.device, q=q, k=k, wq=wq, wk=wk, mask=mask, workspace=workspace)
     _check(load_library().dit_attn_route(_ptr(q), _ptr(k), _ptr(wq), _ptr(wk), T, H, W, heads, d, rope_theta, eps,
@@ -195,11 +209,12 @@ def dit_attn_block_sparse(q, k, v, wq, wk, grid, mask, rope_theta=10000.0, eps=1
     _attn_operands(q, k, v, wq, wk, T * H * W, heads, d)
     nb = -(-(T * H * W) // block)
     _dev(mask, "mask", torch.uint8, (heads, nb, nb))
-    if o is None:
-        o = torch.empty_like(q)
+    with _on_stream(stream):
+        if o is None:
+            o = torch.empty_like(q)
+        if workspace is None:
+            workspace = workspace_for(q, grid)
     _dev(o, "o", torch.bfloat16, tuple(q.shape))
-    if workspace is None:
-        workspace = workspace_for(q, grid)
     _workspace(workspace)
     _on(q.device, q=q, k=k, v=v, wq=wq, wk=wk, mask=mask, o=o, workspace=workspace)
     _check(load_library().dit_attn_block_sparse(_ptr(q), _ptr(k), _ptr(v), _ptr(wq), _ptr(wk), T, H, W, heads, d,
@@ -223,14 +238,15 @@ def dit_attn_joint(q, k, v, wq, wk, q_pos, k_pos, max_pos, rope_theta=10000.0, e
     _attn_operands(q, k, v, wq, wk, nq, heads, d, nk)
     _dev(q_pos, "q_pos", torch.int32, (nq, 3))
     _dev(k_pos, "k_pos", torch.int32, (nk, 3))
-    if o is None:
-        o = torch.empty_like(q)
+    with _on_stream(stream):
+        if o is None:
+            o = torch.empty_like(q)
+        if workspace is None:
+            n = dit_attn_joint_workspace_bytes(nq, nk, heads, d, int(max_pos))
+            if n == 0:
+                raise DitAttnError(DIT_ERR_INVALID_ARG, "invalid sizes for joint workspace sizing")
+            workspace = torch.empty(n, dtype=torch.uint8, device=q.device)
     _dev(o, "o", torch.bfloat16, tuple(q.shape))
-    if workspace is None:
-        n = dit_attn_joint_workspace_bytes(nq, nk, heads, d, int(max_pos))
-        if n == 0:
-            raise DitAttnError(DIT_ERR_INVALID_ARG, "invalid sizes for joint workspace sizing")
-        workspace = torch.empty(n, dtype=torch.uint8, device=q.device)
     _workspace(workspace)
     _on(q.device, q=q, k=k, v=v, wq=wq, wk=wk, q_pos=q_pos, k_pos=k_pos, o=o, workspace=workspace)
     _check(load_library().dit_attn_joint(_ptr(q), _ptr(k), _ptr(v), _ptr(wq), _ptr(wk), _ptr(q_pos), _ptr(k_pos),
@@ -254,7 +270,8 @@ def dit_adaln_modulate(x, shift, scale, eps=1e-6, h=None, stream=None):
     _vec(shift, "shift", hidden)
     _vec(scale, "scale", hidden)
     if h is None:
-        h = torch.empty_like(x)
+        with _on_stream(stream):
+            h = torch.empty_like(x)
     _dev(h, "h", torch.bfloat16, (tokens, hidden))
     _on(x.device, x=x, shift=shift, scale=scale, h=h)
     _check(load_library().dit_adaln_modulate(_ptr(x), _ptr(shift), _ptr(scale), tokens, hidden, eps, _ptr(h),
@@ -271,11 +288,12 @@ def dit_gated_residual(x, y, gate, shift=None, scale=None, eps=1e-6, x_out=None,
     if modulate:
         _vec(shift, "shift", hidden)
         _vec(scale, "scale", hidden)
-    if x_out is None:
-        x_out = torch.empty_like(x)
+    with _on_stream(stream):
+        if x_out is None:
+            x_out = torch.empty_like(x)
+        if modulate and h is None:
+            h = torch.empty_like(x)
     _dev(x_out, "x_out", torch.bfloat16, (tokens, hidden))
-    if modulate and h is None:
-        h = torch.empty_like(x)
     if not modulate:
         h = None
     else:
@@ -294,11 +312,17 @@ def dit_swiglu(gate_up, out=None, stream=None):
         raise ValueError(f"gate_up must hold the gate and up halves: even width (got {width})")
     ffn = width // 2
     if out is None:
-        out = torch.empty((tokens, ffn), dtype=gate_up.dtype, device=gate_up.device)
+        with _on_stream(stream):
+            out = torch.empty((tokens, ffn), dtype=gate_up.dtype, device=gate_up.device)
     _dev(out, "out", torch.bfloat16, (tokens, ffn))
     _on(gate_up.device, gate_up=gate_up, out=out)
     _check(load_library().dit_swiglu(_ptr(gate_up), tokens, ffn, _ptr(out), _stream(stream)))
     return out
+
+
+def dit_attn_set_launch_order(order: int) -> None:
+    """Diagnostic: 0 = the tuned workgroup order of the attention calls, 1 = reversed (no result may change)."""
+    _check(load_library().dit_attn_set_launch_order(int(order)))
 
 
 def dit_attn_last_error() -> str:

@@ -4,13 +4,16 @@
 #include "dit_attn.h"
 #include "dit_block.h"
 
+#include <algorithm>
+#include <atomic>
 #include <cmath>
 #include <cstdarg>
 #include <cstdio>
 #include <cstring>
 #include <map>
+#include <memory>
 #include <mutex>
-#include <string>
+#include <new>
 #include <tuple>
 #include <vector>
 
@@ -18,16 +21,30 @@
 
 namespace {
 
-thread_local std::string g_err;
+// Text of the calling thread's last error.  A fixed buffer: setting it allocates nothing and cannot throw.
+thread_local char g_err[512];
 
 dit_status fail(dit_status s, const char* fmt, ...) {
-  char buf[512];
   va_list ap;
   va_start(ap, fmt);
-  std::vsnprintf(buf, sizeof(buf), fmt, ap);
+  std::vsnprintf(g_err, sizeof(g_err), fmt, ap);
   va_end(ap);
-  g_err = buf;
   return s;
+}
+
+void clear_error() { g_err[0] = '\0'; }
+
+// Runs an entry point's body and turns any C++ exception (host allocation failure in the RoPE table cache
+// being the only one the bodies can raise) into a status: nothing is thrown across the C ABI.
+template <class F>
+dit_status guarded(F&& body) noexcept {
+  try {
+    return body();
+  } catch (const std::bad_alloc&) {
+    return fail(DIT_ERR_HOST, "host memory exhausted");
+  } catch (...) {
+    return fail(DIT_ERR_HOST, "unexpected host-side exception");
+  }
 }
 
 dit_status fail_hip(hipError_t e, const char* what) {
@@ -54,7 +71,8 @@ struct Layout {
   size_t kvf;        // K^ / V^T fragment images [heads][nb] x tile_image_bytes(d) (dense and block-sparse)
   size_t route_pool; // [2][heads][nb][d] f32
   size_t route_score;// [heads][nb][nb] u32 order keys (nb <= dit::route_topk_max_blocks(), else unused)
-  size_t list;       // [heads][nqt][nb] i32
+  size_t list;       // [heads][nqt][nb] i32 visited KV tiles
+  size_t list_flags; // [heads][nqt][nb] u8 slots that keep each visited tile
   size_t list_len;   // [heads][nqt] i32
   size_t perm;       // [heads][nqt][query tile / 128] i32 router block per query-tile slot
   size_t bits;       // [heads][nb][schedule_words(nb)] u64 packed mask rows
@@ -72,15 +90,17 @@ Layout make_layout(const Shape& s) {
   L.route_pool = base;
   L.route_score = base + pool_bytes;
   const size_t list_bytes = align256((size_t)s.heads * s.nqt * s.nb * sizeof(int));
+  const size_t flag_bytes = align256((size_t)s.heads * s.nqt * s.nb);
   const size_t len_bytes = align256((size_t)s.heads * s.nqt * sizeof(int));
   const int group = dit::attn_query_tile(s.d) / dit::kBlock;
   const size_t perm_bytes = align256((size_t)s.heads * s.nqt * group * sizeof(int));
   const size_t bits_bytes = align256((size_t)s.heads * s.nb * dit::schedule_words(s.nb) * sizeof(uint64_t));
   L.list = base;
-  L.list_len = L.list + list_bytes;
+  L.list_flags = L.list + list_bytes;
+  L.list_len = L.list_flags + flag_bytes;
   L.perm = L.list_len + len_bytes;
   L.bits = L.perm + perm_bytes;
-  L.total = base + std::max(pool_bytes + score_bytes, list_bytes + len_bytes + perm_bytes + bits_bytes);
+  L.total = base + std::max(pool_bytes + score_bytes, list_bytes + flag_bytes + len_bytes + perm_bytes + bits_bytes);
   return L;
 }
 
@@ -132,18 +152,35 @@ dit_status check_workspace(const Shape& s, void* ws, size_t ws_bytes, Layout& L)
 // double, C library cos/sin, rounded once to float.  Rows: n0 rows of axis 0 (t), then n1 of axis 1 (h),
 // then n2 of axis 2 (w); each row holds the axis's cos values from float 0 and its sin values from
 // float rope_row_floats(d) / 2.
+//
+// Tables are cached per (rows, theta, head dim), at most kMaxTables of them; a new one evicts the least
+// recently used.  Callers hold a shared reference, so an eviction by another thread never frees a table
+// that is being uploaded.  Allocation failure throws std::bad_alloc, which the entry points' guard turns
+// into DIT_ERR_HOST.
+typedef std::tuple<int, int, int, uint32_t, int> TabKey;
+struct TabEntry {
+  std::shared_ptr<const std::vector<float>> tab;
+  unsigned long long used;
+};
+constexpr size_t kMaxTables = 16;
 std::mutex g_tab_mu;
-std::map<std::tuple<int, int, int, uint32_t, int>, std::vector<float>> g_tabs;
+std::map<TabKey, TabEntry> g_tabs;
+unsigned long long g_tab_clock = 0;
 
-const std::vector<float>& rope_table(int n0, int n1, int n2, float theta, int d) {
+std::shared_ptr<const std::vector<float>> rope_table(int n0, int n1, int n2, float theta, int d) {
   uint32_t tb;
   std::memcpy(&tb, &theta, 4);
-  std::lock_guard<std::mutex> lk(g_tab_mu);
-  auto key = std::make_tuple(n0, n1, n2, tb, d);
-  auto it = g_tabs.find(key);
-  if (it != g_tabs.end()) return it->second;
+  const TabKey key = std::make_tuple(n0, n1, n2, tb, d);
+  {
+    std::lock_guard<std::mutex> lk(g_tab_mu);
+    auto it = g_tabs.find(key);
+    if (it != g_tabs.end()) {
+      it->second.used = ++g_tab_clock;
+      return it->second.tab;
+    }
+  }
   const int rs = dit::rope_row_floats(d);
-  std::vector<float> tab((size_t)(n0 + n1 + n2) * rs, 0.0f);
+  auto tab = std::make_shared<std::vector<float>>((size_t)(n0 + n1 + n2) * rs, 0.0f);
   const int npos[3] = {n0, n1, n2};
   int row = 0;
   for (int a = 0; a < 3; ++a) {
@@ -152,20 +189,64 @@ const std::vector<float>& rope_table(int n0, int n1, int n2, float theta, int d)
       for (int i = 0; i < width / 2; ++i) {
         const double inv = std::pow((double)theta, -2.0 * i / (double)width);
         const double ang = (double)p * inv;
-        tab[(size_t)row * rs + i] = (float)std::cos(ang);
-        tab[(size_t)row * rs + rs / 2 + i] = (float)std::sin(ang);
+        (*tab)[(size_t)row * rs + i] = (float)std::cos(ang);
+        (*tab)[(size_t)row * rs + rs / 2 + i] = (float)std::sin(ang);
       }
     }
   }
-  return g_tabs.emplace(key, std::move(tab)).first->second;
+  std::lock_guard<std::mutex> lk(g_tab_mu);
+  while (g_tabs.size() >= kMaxTables) {
+    auto lru = g_tabs.begin();
+    for (auto it = g_tabs.begin(); it != g_tabs.end(); ++it)
+      if (it->second.used < lru->second.used) lru = it;
+    g_tabs.erase(lru);
+  }
+  TabEntry& e = g_tabs[key];   // another thread may have built the same table meanwhile: same contents
+  e.tab = tab;
+  e.used = ++g_tab_clock;
+  return tab;
 }
 
-dit_status upload_table(const Shape& s, float theta, void* ws, const Layout& L, hipStream_t st) {
-  const std::vector<float>& tab = rope_table(s.T, s.H, s.W, theta, s.d);
-  hipError_t e = hipMemcpyAsync((char*)ws + L.tab, tab.data(), tab.size() * sizeof(float), hipMemcpyHostToDevice, st);
+// Host -> device copy of a table.  The source is pageable host memory, which the runtime has finished
+// reading when the call returns, so the table may be evicted from the cache right after.
+dit_status upload(const std::vector<float>& tab, void* dst, hipStream_t st) {
+  hipError_t e = hipMemcpyAsync(dst, tab.data(), tab.size() * sizeof(float), hipMemcpyHostToDevice, st);
   if (e != hipSuccess) return fail_hip(e, "hipMemcpyAsync(rope table)");
   return DIT_OK;
 }
+
+dit_status upload_table(const Shape& s, float theta, void* ws, const Layout& L, hipStream_t st) {
+  const auto tab = rope_table(s.T, s.H, s.W, theta, s.d);
+  return upload(*tab, (char*)ws + L.tab, st);
+}
+
+// [p, p + bytes) and [q, q + bytes2) share a byte.
+bool overlaps(const void* p, size_t bytes, const void* q, size_t bytes2) {
+  const uintptr_t a = (uintptr_t)p, b = (uintptr_t)q;
+  return a < b + bytes2 && b < a + bytes;
+}
+
+// A buffer of a call: where it starts, its size in bytes, its name, and whether the call writes it.
+struct Buf {
+  const void* p;
+  size_t bytes;
+  const char* name;
+  bool written;
+};
+
+// Every buffer the call writes (outputs and workspace) must be disjoint from every other buffer of the
+// call; read-only inputs may share memory with each other.
+template <size_t K>
+dit_status check_disjoint(const Buf (&b)[K]) {
+  for (size_t i = 0; i < K; ++i)
+    for (size_t j = i + 1; j < K; ++j)
+      if ((b[i].written || b[j].written) && b[i].p && b[j].p && overlaps(b[i].p, b[i].bytes, b[j].p, b[j].bytes))
+        return fail(DIT_ERR_INVALID_ARG, "%s overlaps %s", b[i].name, b[j].name);
+  return DIT_OK;
+}
+
+// Workgroup order of the attention calls (diagnostic; see dit_attn_set_launch_order).
+std::atomic<int> g_launch_order{0};
 
 dit::GridDesc grid_desc(const Shape& s) {
   dit::GridDesc g;
@@ -202,6 +283,7 @@ dit::AttnArgs attn_args(const Shape& s, const void* q, const void* k, const void
   a.nqt = s.nqt;
   a.total = s.heads * s.nqt;
   a.per_xcd = (a.total + 7) / 8;
+  a.order = g_launch_order.load(std::memory_order_relaxed);
   a.nb = s.nb;
   return a;
 }
@@ -261,13 +343,25 @@ dit_status check_joint_shape(int nq, int nk, int heads, int head_dim, int max_po
 
 extern "C" {
 
-size_t dit_attn_workspace_bytes(int T, int H, int W, int heads, int head_dim, int block) {
+size_t dit_attn_workspace_bytes(int T, int H, int W, int heads, int head_dim, int block, float sparsity) {
+  // Computes a size only: the caller's last error is left as it was.
+  char saved[sizeof(g_err)];
+  std::memcpy(saved, g_err, sizeof(g_err));
   Shape s;
-  std::string saved = g_err;
   const dit_status st = check_shape(T, H, W, heads, head_dim, s);
-  g_err = saved;
+  std::memcpy(g_err, saved, sizeof(g_err));
   if (st != DIT_OK || block != dit::kBlock) return 0;
+  if (!std::isfinite(sparsity) || sparsity < 0.f || sparsity >= 1.f) return 0;
+  // The block-sparse lists are sized for any mask (block_sparse accepts masks from any source), so the
+  // size does not depend on the sparsity.
   return make_layout(s).total;
+}
+
+dit_status dit_attn_set_launch_order(int order) {
+  clear_error();
+  if (order != 0 && order != 1) return fail(DIT_ERR_INVALID_ARG, "launch order must be 0 or 1 (got %d)", order);
+  g_launch_order.store(order, std::memory_order_relaxed);
+  return DIT_OK;
 }
 
 int dit_attn_keep_count(int nb, float sparsity) {
@@ -278,101 +372,127 @@ int dit_attn_keep_count(int nb, float sparsity) {
 dit_status dit_attn_dense(const void* q, const void* k, const void* v, const float* wq, const float* wk, int T, int H,
                           int W, int heads, int head_dim, float rope_theta, float eps, void* o, void* workspace,
                           size_t workspace_bytes, void* hip_stream) {
-  g_err.clear();
-  Shape s;
-  dit_status st = check_shape(T, H, W, heads, head_dim, s);
-  if (st != DIT_OK) return st;
-  if ((st = check_common(q, k, wq, wk, rope_theta, eps)) != DIT_OK) return st;
-  if (!v || !o) return fail(DIT_ERR_INVALID_ARG, "null v or o");
-  if (!aligned16(v) || !aligned16(o)) return fail(DIT_ERR_INVALID_ARG, "v and o must be 16-byte aligned");
-  Layout L;
-  if ((st = check_workspace(s, workspace, workspace_bytes, L)) != DIT_OK) return st;
-  hipStream_t stream = (hipStream_t)hip_stream;
-  if ((st = upload_table(s, rope_theta, workspace, L, stream)) != DIT_OK) return st;
-  const dit::AttnArgs a = attn_args(s, q, k, v, wq, wk, eps, o, workspace, L);
-  const hipError_t e = dit::launch_attn_dense(a, stream);
-  if (e != hipSuccess) return fail_hip(e, "attention kernel launch");
-  return DIT_OK;
+  clear_error();
+  return guarded([&]() -> dit_status {
+    Shape s;
+    dit_status st = check_shape(T, H, W, heads, head_dim, s);
+    if (st != DIT_OK) return st;
+    if ((st = check_common(q, k, wq, wk, rope_theta, eps)) != DIT_OK) return st;
+    if (!v || !o) return fail(DIT_ERR_INVALID_ARG, "null v or o");
+    if (!aligned16(v) || !aligned16(o)) return fail(DIT_ERR_INVALID_ARG, "v and o must be 16-byte aligned");
+    Layout L;
+    if ((st = check_workspace(s, workspace, workspace_bytes, L)) != DIT_OK) return st;
+    const size_t tb = (size_t)s.N * s.heads * s.d * 2, wb = (size_t)s.d * 4;
+    const Buf bufs[] = {{q, tb, "q", false},  {k, tb, "k", false},   {v, tb, "v", false},
+                        {wq, wb, "wq", false}, {wk, wb, "wk", false}, {o, tb, "o", true},
+                        {workspace, L.total, "workspace", true}};
+    if ((st = check_disjoint(bufs)) != DIT_OK) return st;
+    hipStream_t stream = (hipStream_t)hip_stream;
+    if ((st = upload_table(s, rope_theta, workspace, L, stream)) != DIT_OK) return st;
+    const dit::AttnArgs a = attn_args(s, q, k, v, wq, wk, eps, o, workspace, L);
+    const hipError_t e = dit::launch_attn_dense(a, stream);
+    if (e != hipSuccess) return fail_hip(e, "attention kernel launch");
+    return DIT_OK;
+  });
 }
 
 dit_status dit_attn_route(const void* q, const void* k, const float* wq, const float* wk, int T, int H, int W,
                           int heads, int head_dim, float rope_theta, float eps, float sparsity, int block,
                           unsigned char* mask, void* workspace, size_t workspace_bytes, void* hip_stream) {
-  g_err.clear();
-  Shape s;
-  dit_status st = check_shape(T, H, W, heads, head_dim, s);
-  if (st != DIT_OK) return st;
-  if (block != dit::kBlock) return fail(DIT_ERR_UNSUPPORTED, "block %d is not supported (only 128)", block);
-  if ((st = check_common(q, k, wq, wk, rope_theta, eps)) != DIT_OK) return st;
-  if (!std::isfinite(sparsity) || sparsity < 0.f || sparsity >= 1.f)
-    return fail(DIT_ERR_INVALID_ARG, "sparsity must be in [0, 1)");
-  if (!mask) return fail(DIT_ERR_INVALID_ARG, "null mask");
-  Layout L;
-  if ((st = check_workspace(s, workspace, workspace_bytes, L)) != DIT_OK) return st;
-  hipStream_t stream = (hipStream_t)hip_stream;
-  if ((st = upload_table(s, rope_theta, workspace, L, stream)) != DIT_OK) return st;
-  dit::RouteArgs a{};
-  a.q = (const uint16_t*)q;
-  a.k = (const uint16_t*)k;
-  a.wq = wq;
-  a.wk = wk;
-  a.rope = (const float*)((const char*)workspace + L.tab);
-  a.g = grid_desc(s);
-  a.eps = eps;
-  a.nb = s.nb;
-  a.keep = keep_count(s.nb, sparsity);
-  a.pooled = (float*)((char*)workspace + L.route_pool);
-  a.scores = (uint32_t*)((char*)workspace + L.route_score);
-  a.mask = mask;
-  a.head_dim = s.d;
-  const hipError_t e = dit::launch_route(a, stream);
-  if (e != hipSuccess) return fail_hip(e, "router kernel launch");
-  return DIT_OK;
+  clear_error();
+  return guarded([&]() -> dit_status {
+    Shape s;
+    dit_status st = check_shape(T, H, W, heads, head_dim, s);
+    if (st != DIT_OK) return st;
+    if (block != dit::kBlock) return fail(DIT_ERR_UNSUPPORTED, "block %d is not supported (only 128)", block);
+    if ((st = check_common(q, k, wq, wk, rope_theta, eps)) != DIT_OK) return st;
+    if (!std::isfinite(sparsity) || sparsity < 0.f || sparsity >= 1.f)
+      return fail(DIT_ERR_INVALID_ARG, "sparsity must be in [0, 1)");
+    if (!mask) return fail(DIT_ERR_INVALID_ARG, "null mask");
+    Layout L;
+    if ((st = check_workspace(s, workspace, workspace_bytes, L)) != DIT_OK) return st;
+    const size_t tb = (size_t)s.N * s.heads * s.d * 2, wb = (size_t)s.d * 4;
+    const Buf bufs[] = {{q, tb, "q", false},   {k, tb, "k", false},
+                        {wq, wb, "wq", false},  {wk, wb, "wk", false},
+                        {mask, (size_t)s.heads * s.nb * s.nb, "mask", true},
+                        {workspace, L.total, "workspace", true}};
+    if ((st = check_disjoint(bufs)) != DIT_OK) return st;
+    hipStream_t stream = (hipStream_t)hip_stream;
+    if ((st = upload_table(s, rope_theta, workspace, L, stream)) != DIT_OK) return st;
+    dit::RouteArgs a{};
+    a.q = (const uint16_t*)q;
+    a.k = (const uint16_t*)k;
+    a.wq = wq;
+    a.wk = wk;
+    a.rope = (const float*)((const char*)workspace + L.tab);
+    a.g = grid_desc(s);
+    a.eps = eps;
+    a.nb = s.nb;
+    a.keep = keep_count(s.nb, sparsity);
+    a.pooled = (float*)((char*)workspace + L.route_pool);
+    a.scores = (uint32_t*)((char*)workspace + L.route_score);
+    a.mask = mask;
+    a.head_dim = s.d;
+    const hipError_t e = dit::launch_route(a, stream);
+    if (e != hipSuccess) return fail_hip(e, "router kernel launch");
+    return DIT_OK;
+  });
 }
 
 dit_status dit_attn_block_sparse(const void* q, const void* k, const void* v, const float* wq, const float* wk, int T,
                                  int H, int W, int heads, int head_dim, float rope_theta, float eps, int block,
                                  const unsigned char* mask, void* o, void* workspace, size_t workspace_bytes,
                                  void* hip_stream) {
-  g_err.clear();
-  Shape s;
-  dit_status st = check_shape(T, H, W, heads, head_dim, s);
-  if (st != DIT_OK) return st;
-  if (block != dit::kBlock) return fail(DIT_ERR_UNSUPPORTED, "block %d is not supported (only 128)", block);
-  if ((st = check_common(q, k, wq, wk, rope_theta, eps)) != DIT_OK) return st;
-  if (!v || !o || !mask) return fail(DIT_ERR_INVALID_ARG, "null v, o or mask");
-  if (!aligned16(v) || !aligned16(o)) return fail(DIT_ERR_INVALID_ARG, "v and o must be 16-byte aligned");
-  Layout L;
-  if ((st = check_workspace(s, workspace, workspace_bytes, L)) != DIT_OK) return st;
-  hipStream_t stream = (hipStream_t)hip_stream;
-  if ((st = upload_table(s, rope_theta, workspace, L, stream)) != DIT_OK) return st;
-  dit::ScheduleArgs c{};
-  c.mask = mask;
-  c.bits = (unsigned long long*)((char*)workspace + L.bits);
-  c.perm = (int*)((char*)workspace + L.perm);
-  c.list = (int*)((char*)workspace + L.list);
-  c.list_len = (int*)((char*)workspace + L.list_len);
-  c.heads = s.heads;
-  c.nb = s.nb;
-  c.nqt = s.nqt;
-  c.group = dit::attn_query_tile(s.d) / dit::kBlock;
-  c.words = dit::schedule_words(s.nb);
-  hipError_t e = dit::launch_sparse_schedule(c, stream);
-  if (e != hipSuccess) return fail_hip(e, "block-sparse schedule launch");
-  dit::AttnArgs a = attn_args(s, q, k, v, wq, wk, eps, o, workspace, L);
-  a.list = c.list;
-  a.list_len = c.list_len;
-  a.perm = c.perm;
-  e = dit::launch_attn_sparse(a, stream);
-  if (e != hipSuccess) return fail_hip(e, "sparse attention kernel launch");
-  return DIT_OK;
+  clear_error();
+  return guarded([&]() -> dit_status {
+    Shape s;
+    dit_status st = check_shape(T, H, W, heads, head_dim, s);
+    if (st != DIT_OK) return st;
+    if (block != dit::kBlock) return fail(DIT_ERR_UNSUPPORTED, "block %d is not supported (only 128)", block);
+    if ((st = check_common(q, k, wq, wk, rope_theta, eps)) != DIT_OK) return st;
+    if (!v || !o || !mask) return fail(DIT_ERR_INVALID_ARG, "null v, o or mask");
+    if (!aligned16(v) || !aligned16(o)) return fail(DIT_ERR_INVALID_ARG, "v and o must be 16-byte aligned");
+    Layout L;
+    if ((st = check_workspace(s, workspace, workspace_bytes, L)) != DIT_OK) return st;
+    const size_t tb = (size_t)s.N * s.heads * s.d * 2, wb = (size_t)s.d * 4;
+    const Buf bufs[] = {{q, tb, "q", false},   {k, tb, "k", false}, {v, tb, "v", false},
+                        {wq, wb, "wq", false},  {wk, wb, "wk", false},
+                        {mask, (size_t)s.heads * s.nb * s.nb, "mask", false},
+                        {o, tb, "o", true},     {workspace, L.total, "workspace", true}};
+    if ((st = check_disjoint(bufs)) != DIT_OK) return st;
+    hipStream_t stream = (hipStream_t)hip_stream;
+    if ((st = upload_table(s, rope_theta, workspace, L, stream)) != DIT_OK) return st;
+    dit::ScheduleArgs c{};
+    c.mask = mask;
+    c.bits = (unsigned long long*)((char*)workspace + L.bits);
+    c.perm = (int*)((char*)workspace + L.perm);
+    c.list = (int*)((char*)workspace + L.list);
+    c.list_flags = (unsigned char*)((char*)workspace + L.list_flags);
+    c.list_len = (int*)((char*)workspace + L.list_len);
+    c.heads = s.heads;
+    c.nb = s.nb;
+    c.nqt = s.nqt;
+    c.group = dit::attn_query_tile(s.d) / dit::kBlock;
+    c.words = dit::schedule_words(s.nb);
+    hipError_t e = dit::launch_sparse_schedule(c, stream);
+    if (e != hipSuccess) return fail_hip(e, "block-sparse schedule launch");
+    dit::AttnArgs a = attn_args(s, q, k, v, wq, wk, eps, o, workspace, L);
+    a.list = c.list;
+    a.list_flags = c.list_flags;
+    a.list_len = c.list_len;
+    a.perm = c.perm;
+    e = dit::launch_attn_sparse(a, stream);
+    if (e != hipSuccess) return fail_hip(e, "sparse attention kernel launch");
+    return DIT_OK;
+  });
 }
 
 size_t dit_attn_joint_workspace_bytes(int nq, int nk, int heads, int head_dim, int max_pos) {
+  char saved[sizeof(g_err)];
+  std::memcpy(saved, g_err, sizeof(g_err));
   JointShape j;
-  std::string saved = g_err;
   const dit_status st = check_joint_shape(nq, nk, heads, head_dim, max_pos, j);
-  g_err = saved;
+  std::memcpy(g_err, saved, sizeof(g_err));
   if (st != DIT_OK) return 0;
   return make_joint_layout(j).total;
 }
@@ -381,56 +501,67 @@ dit_status dit_attn_joint(const void* q, const void* k, const void* v, const flo
                           const int* q_pos, const int* k_pos, int nq, int nk, int heads, int head_dim, int max_pos,
                           float rope_theta, float eps, void* o, void* workspace, size_t workspace_bytes,
                           void* hip_stream) {
-  g_err.clear();
-  JointShape j;
-  dit_status st = check_joint_shape(nq, nk, heads, head_dim, max_pos, j);
-  if (st != DIT_OK) return st;
-  if ((st = check_common(q, k, wq, wk, rope_theta, eps)) != DIT_OK) return st;
-  if (!v || !o || !q_pos || !k_pos) return fail(DIT_ERR_INVALID_ARG, "null v, o, q_pos or k_pos");
-  if (!aligned16(v) || !aligned16(o)) return fail(DIT_ERR_INVALID_ARG, "v and o must be 16-byte aligned");
-  if (((uintptr_t)q_pos & 3u) || ((uintptr_t)k_pos & 3u))
-    return fail(DIT_ERR_INVALID_ARG, "q_pos and k_pos must be 4-byte aligned");
-  const JointLayout L = make_joint_layout(j);
-  if (!workspace) return fail(DIT_ERR_WORKSPACE, "workspace is null (need %zu bytes)", L.total);
-  if (workspace_bytes < L.total)
-    return fail(DIT_ERR_WORKSPACE, "workspace has %zu bytes, need %zu", workspace_bytes, L.total);
-  if (((uintptr_t)workspace & 255u) != 0) return fail(DIT_ERR_INVALID_ARG, "workspace must be 256-byte aligned");
-  hipStream_t stream = (hipStream_t)hip_stream;
-  // rows p = 0 .. max_pos-1 of each axis section; at head dim 96 the three axes have the same width and
-  // share one section
-  const std::vector<float>& tab = j.sections == 1 ? rope_table(max_pos, 0, 0, rope_theta, j.d)
-                                                  : rope_table(max_pos, max_pos, max_pos, rope_theta, j.d);
-  hipError_t e = hipMemcpyAsync((char*)workspace + L.tab, tab.data(), tab.size() * sizeof(float),
-                                hipMemcpyHostToDevice, stream);
-  if (e != hipSuccess) return fail_hip(e, "hipMemcpyAsync(rope table)");
-  dit::AttnArgs a{};
-  a.q = (const uint16_t*)q;
-  a.k = (const uint16_t*)k;
-  a.v = (const uint16_t*)v;
-  a.wq = wq;
-  a.wk = wk;
-  a.rope = (const float*)((const char*)workspace + L.tab);
-  a.kvf = (uint16_t*)((char*)workspace + L.kvf);
-  a.o = (uint16_t*)o;
-  a.g = dit::GridDesc{};
-  a.g.heads = heads;
-  a.nq = nq;
-  a.nk = nk;
-  a.q_pos = q_pos;
-  a.k_pos = k_pos;
-  a.max_pos = max_pos;
-  for (int i = 0; i < 3; ++i) a.rope_sec[i] = j.sections == 1 ? 0 : i * max_pos;
-  a.head_dim = j.d;
-  a.qscale = (float)(1.4426950408889634 / std::sqrt((double)j.d));
-  a.eps = eps;
-  a.nqt = j.nqt;
-  a.total = heads * j.nqt;
-  a.per_xcd = (a.total + 7) / 8;
-  a.nb = j.nb;
-  e = dit::launch_attn_dense(a, stream);
-  if (e != hipSuccess) return fail_hip(e, "joint attention kernel launch");
-  return DIT_OK;
+  clear_error();
+  return guarded([&]() -> dit_status {
+    JointShape j;
+    dit_status st = check_joint_shape(nq, nk, heads, head_dim, max_pos, j);
+    if (st != DIT_OK) return st;
+    if ((st = check_common(q, k, wq, wk, rope_theta, eps)) != DIT_OK) return st;
+    if (!v || !o || !q_pos || !k_pos) return fail(DIT_ERR_INVALID_ARG, "null v, o, q_pos or k_pos");
+    if (!aligned16(v) || !aligned16(o)) return fail(DIT_ERR_INVALID_ARG, "v and o must be 16-byte aligned");
+    if (((uintptr_t)q_pos & 3u) || ((uintptr_t)k_pos & 3u))
+      return fail(DIT_ERR_INVALID_ARG, "q_pos and k_pos must be 4-byte aligned");
+    const JointLayout L = make_joint_layout(j);
+    if (!workspace) return fail(DIT_ERR_WORKSPACE, "workspace is null (need %zu bytes)", L.total);
+    if (workspace_bytes < L.total)
+      return fail(DIT_ERR_WORKSPACE, "workspace has %zu bytes, need %zu", workspace_bytes, L.total);
+    if (((uintptr_t)workspace & 255u) != 0) return fail(DIT_ERR_INVALID_ARG, "workspace must be 256-byte aligned");
+    const size_t qb = (size_t)nq * heads * head_dim * 2, kb = (size_t)nk * heads * head_dim * 2;
+    const size_t wb = (size_t)head_dim * 4;
+    const Buf bufs[] = {{q, qb, "q", false},   {k, kb, "k", false},   {v, kb, "v", false},
+                        {wq, wb, "wq", false},  {wk, wb, "wk", false},
+                        {q_pos, (size_t)nq * 12, "q_pos", false},
+                        {k_pos, (size_t)nk * 12, "k_pos", false},
+                        {o, qb, "o", true},     {workspace, L.total, "workspace", true}};
+    if ((st = check_disjoint(bufs)) != DIT_OK) return st;
+    hipStream_t stream = (hipStream_t)hip_stream;
+    // rows p = 0 .. max_pos-1 of each axis section; at head dim 96 the three axes have the same width and
+    // share one section
+    const auto tab = j.sections == 1 ? rope_table(max_pos, 0, 0, rope_theta, j.d)
+                                     : rope_table(max_pos, max_pos, max_pos, rope_theta, j.d);
+    if ((st = upload(*tab, (char*)workspace + L.tab, stream)) != DIT_OK) return st;
+    dit::AttnArgs a{};
+    a.q = (const uint16_t*)q;
+    a.k = (const uint16_t*)k;
+    a.v = (const uint16_t*)v;
+    a.wq = wq;
+    a.wk = wk;
+    a.rope = (const float*)((const char*)workspace + L.tab);
+    a.kvf = (uint16_t*)((char*)workspace + L.kvf);
+    a.o = (uint16_t*)o;
+    a.g = dit::GridDesc{};
+    a.g.heads = heads;
+    a.nq = nq;
+    a.nk = nk;
+    a.q_pos = q_pos;
+    a.k_pos = k_pos;
+    a.max_pos = max_pos;
+    for (int i = 0; i < 3; ++i) a.rope_sec[i] = j.sections == 1 ? 0 : i * max_pos;
+    a.head_dim = j.d;
+    a.qscale = (float)(1.4426950408889634 / std::sqrt((double)j.d));
+    a.eps = eps;
+    a.nqt = j.nqt;
+    a.total = heads * j.nqt;
+    a.per_xcd = (a.total + 7) / 8;
+    a.order = g_launch_order.load(std::memory_order_relaxed);
+    a.nb = j.nb;
+    const hipError_t e = dit::launch_attn_dense(a, stream);
+    if (e != hipSuccess) return fail_hip(e, "joint attention kernel launch");
+    return DIT_OK;
+  });
 }
+
+}  // extern "C"
 
 // ------------------------------------------------------------------------------------------------
 // Operators around attention (dit_block.h)
@@ -438,12 +569,6 @@ dit_status dit_attn_joint(const void* q, const void* k, const void* v, const flo
 namespace {
 
 constexpr int kMaxHidden = 8192;
-
-// [p, p + bytes) and [q, q + bytes2) share a byte.
-bool overlaps(const void* p, size_t bytes, const void* q, size_t bytes2) {
-  const uintptr_t a = (uintptr_t)p, b = (uintptr_t)q;
-  return a < b + bytes2 && b < a + bytes;
-}
 
 dit_status check_rows(long long tokens, int width, const char* what) {
   if (tokens < 0) return fail(DIT_ERR_INVALID_ARG, "tokens must be >= 0 (got %lld)", tokens);
@@ -454,9 +579,12 @@ dit_status check_rows(long long tokens, int width, const char* what) {
 
 }  // namespace
 
+// These calls allocate nothing on the host; no C++ exception can arise in them.
+extern "C" {
+
 dit_status dit_adaln_modulate(const void* x, const float* shift, const float* scale, long long tokens, int hidden,
                               float eps, void* h, void* hip_stream) {
-  g_err.clear();
+  clear_error();
   dit_status st = check_rows(tokens, hidden, "hidden");
   if (st != DIT_OK) return st;
   if (hidden > kMaxHidden) return fail(DIT_ERR_UNSUPPORTED, "hidden %d exceeds %d", hidden, kMaxHidden);
@@ -482,7 +610,7 @@ dit_status dit_adaln_modulate(const void* x, const float* shift, const float* sc
 
 dit_status dit_gated_residual(const void* x, const void* y, const float* gate, const float* shift, const float* scale,
                               long long tokens, int hidden, float eps, void* x_out, void* h, void* hip_stream) {
-  g_err.clear();
+  clear_error();
   dit_status st = check_rows(tokens, hidden, "hidden");
   if (st != DIT_OK) return st;
   if (hidden > kMaxHidden) return fail(DIT_ERR_UNSUPPORTED, "hidden %d exceeds %d", hidden, kMaxHidden);
@@ -516,7 +644,7 @@ dit_status dit_gated_residual(const void* x, const void* y, const float* gate, c
 }
 
 dit_status dit_swiglu(const void* gate_up, long long tokens, int ffn, void* out, void* hip_stream) {
-  g_err.clear();
+  clear_error();
   dit_status st = check_rows(tokens, ffn, "ffn");
   if (st != DIT_OK) return st;
   if (ffn > (1 << 28)) return fail(DIT_ERR_UNSUPPORTED, "ffn %d too large", ffn);
@@ -535,6 +663,6 @@ dit_status dit_swiglu(const void* gate_up, long long tokens, int ffn, void* out,
   return DIT_OK;
 }
 
-const char* dit_attn_last_error(void) { return g_err.c_str(); }
+const char* dit_attn_last_error(void) { return g_err; }
 
 }  // extern "C"

@@ -25,8 +25,8 @@
 //  * KV tiles are double-buffered in LDS: the next tile's fragment image is in
 //    flight (global->LDS, no registers, issued as inline assembly so that the
 //    fragment reads get graded LDS waits) while the current one is consumed.
-//    Block-sparse tiles take their KV tile and flags from a per-tile list whose
-//    entries are loaded two visits ahead.
+//    Block-sparse tiles take their KV tile and slot flags from per-tile lists
+//    whose entries are loaded two visits ahead.
 //  * S^T = K^ Q^T with v_mfma_f32_32x32x16_bf16 (keys on rows, queries on columns):
 //    each lane holds one query column, so the softmax row statistics need only
 //    in-lane reductions plus one permlane32 swap, and the S^T accumulator is
@@ -447,9 +447,9 @@ __device__ __forceinline__ void store_o(const AttnArgs& a, int head, int qt, int
 // Shared setup of both kernels: workgroup -> (head, query tile) with the XCD-aware order, tile list.
 struct TileIter {
   int head, qt, ntiles;
-  const int* lst;
-  __device__ __forceinline__ int tile(int it, bool sparse) const { return sparse ? (lst[it] & 0xffffff) : it; }
-  __device__ __forceinline__ int flags(int it, bool sparse) const { return sparse ? (lst[it] >> 24) : 0xff; }
+  const int* lst;               // block-sparse: visited KV tiles (plain indices below nb)
+  const unsigned char* flg;     // block-sparse: slots of the query tile that keep each visited tile
+  __device__ __forceinline__ int tile(int it, bool sparse) const { return sparse ? lst[it] : it; }
 };
 
 template <bool SPARSE>
@@ -459,16 +459,19 @@ __device__ __forceinline__ bool tile_iter(const AttnArgs& a, TileIter& ti) {
   // tiles of a head visit different KV subsets and drift apart, so L2 sharing is weak; consecutive
   // launch indices keep the whole chip on about one head at a time instead, whose fragment image is
   // then re-read from the last-level cache rather than HBM (3% faster on the 10 s video layer).
-  const int logical = SPARSE ? (int)blockIdx.x : (int)(blockIdx.x & 7) * a.per_xcd + (int)(blockIdx.x >> 3);
+  int logical = SPARSE ? (int)blockIdx.x : (int)(blockIdx.x & 7) * a.per_xcd + (int)(blockIdx.x >> 3);
   if (logical >= a.total) return false;
+  if (a.order != 0) logical = a.total - 1 - logical;   // diagnostic reversed order: same work, other timing
   ti.head = logical / a.nqt;
   ti.qt = logical - ti.head * a.nqt;
   if constexpr (SPARSE) {
     ti.ntiles = a.list_len[logical];
     ti.lst = a.list + (size_t)logical * a.nb;
+    ti.flg = a.list_flags + (size_t)logical * a.nb;
   } else {
     ti.ntiles = (a.nk + BK - 1) / BK;
     ti.lst = nullptr;
+    ti.flg = nullptr;
   }
   return true;
 }
@@ -483,8 +486,9 @@ __global__ void __launch_bounds__(256) kv_prep_kernel(AttnArgs a) {
   __shared__ __attribute__((aligned(16))) uint16_t rk[BK * D];
   __shared__ __attribute__((aligned(16))) uint16_t rv[BK * D];
   __shared__ __attribute__((aligned(16))) float sW[D];
-  const int tile = blockIdx.x, head = blockIdx.y, tid = threadIdx.x;
-  const int N = a.nk;
+  const int tile = a.order != 0 ? (int)(gridDim.x - 1 - blockIdx.x) : (int)blockIdx.x;
+  const int head = a.order != 0 ? (int)(gridDim.y - 1 - blockIdx.y) : (int)blockIdx.y;
+  const int tid = threadIdx.x, N = a.nk;
   if (tid < D) sW[tid] = a.wk[tid];
   for (int i = tid; i < BK * CH; i += 256) {
     const int row = i / CH, c = i - CH * row;
@@ -675,23 +679,29 @@ __device__ __forceinline__ void attn_kernel_body(const AttnArgs& a, uint16_t* sK
 #pragma unroll
     for (int db = 0; db < DB; ++db) acc[qb][db] = f32x16{};
   }
-  // Block-sparse: the list entries of the current and the next tile are carried in registers, and the
-  // entry two tiles ahead is loaded at the top of each iteration; only the tile barrier's vmcnt(0) waits
-  // for it, so no visit stalls on a list read before it can start the next copy and its own MFMAs.
-  int e_cur = 0, e_nxt = 0;
+  // Block-sparse: the list entries (tile and slot flags) of the current and the next tile are carried in
+  // registers, and those two tiles ahead are loaded at the top of each iteration; only the tile barrier's
+  // vmcnt(0) waits for them, so no visit stalls on a list read before it can start the next copy and its
+  // own MFMAs.  Tile indices and flags come from separate arrays: a copy address is formed from a plain
+  // tile index, with no field to mask off.
+  int e_cur = 0, e_nxt = 0, f_cur = 0, f_nxt = 0;
   if constexpr (SPARSE) {
     e_cur = nt > 0 ? ti.lst[0] : 0;
     e_nxt = nt > 1 ? ti.lst[1] : 0;
+    f_cur = nt > 0 ? ti.flg[0] : 0;
+    f_nxt = nt > 1 ? ti.flg[1] : 0;
   }
   tile_barrier();
   for (int it = 0; it < nt; ++it) {
-    int e_nn = 0;
-    if constexpr (SPARSE) e_nn = it + 2 < nt ? ti.lst[it + 2] : 0;
-    const int st = it & 1, tile = SPARSE ? (e_cur & 0xffffff) : it;
+    int e_nn = 0, f_nn = 0;
+    if constexpr (SPARSE) {
+      e_nn = it + 2 < nt ? ti.lst[it + 2] : 0;
+      f_nn = it + 2 < nt ? ti.flg[it + 2] : 0;
+    }
+    const int st = it & 1, tile = SPARSE ? e_cur : it;
     if (it + 1 < nt)
-      dma_tile<D>(img + (size_t)(SPARSE ? (e_nxt & 0xffffff) : it + 1) * TILE, wave, lane,
-                           sKV + (st ^ 1) * TILE);
-    const int flags = SPARSE ? (e_cur >> 24) : 0xff;
+      dma_tile<D>(img + (size_t)(SPARSE ? e_nxt : it + 1) * TILE, wave, lane, sKV + (st ^ 1) * TILE);
+    const int flags = SPARSE ? f_cur : 0xff;
     int qm = 0;
 #pragma unroll
     for (int qb = 0; qb < QB; ++qb) qm |= ((flags >> rbit[qb]) & 1) << qb;
@@ -712,6 +722,8 @@ __device__ __forceinline__ void attn_kernel_body(const AttnArgs& a, uint16_t* sK
     tile_barrier();
     e_cur = e_nxt;
     e_nxt = e_nn;
+    f_cur = f_nxt;
+    f_nxt = f_nn;
   }
   store_o<D, QB, BQ, SPARSE>(a, ti.head, ti.qt, wave, lane, acc, l);
 }

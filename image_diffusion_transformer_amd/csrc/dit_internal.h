@@ -61,8 +61,10 @@ struct AttnArgs {
   int nqt;                // query tiles per head
   int total;              // heads * nqt
   int per_xcd;            // ceil(total / 8)
+  int order;              // workgroup order: 0 = the tuned one, 1 = reversed (results must not change)
   // block-sparse iteration lists (null for dense)
-  const int* list;        // [heads][nqt][nb]: kv block | (router-block flags << 24)
+  const int* list;        // [heads][nqt][nb]: visited KV tiles, ascending (plain tile indices < nb)
+  const unsigned char* list_flags;  // [heads][nqt][nb]: bit s = slot s of the query tile keeps that KV tile
   const int* list_len;    // [heads][nqt]
   const int* perm;        // [heads][nqt][BQ/128]: router block in each slot of a query tile, -1 = none
   int nb;                 // 128-key tiles: ceil(nk / 128)
@@ -88,7 +90,8 @@ struct ScheduleArgs {
   const unsigned char* mask;   // [heads][nb][nb]
   unsigned long long* bits;    // [heads][nb][words] packed mask rows
   int* perm;                   // [heads][nqt][group] router block of each query-tile slot, -1 = none
-  int* list;                   // [heads][nqt][nb]
+  int* list;                   // [heads][nqt][nb] visited KV tiles
+  unsigned char* list_flags;   // [heads][nqt][nb] slots of the query tile that keep each visited tile
   int* list_len;               // [heads][nqt]
   int heads, nb, nqt, group;   // group = router blocks per query tile (<= 8)
   int words;                   // schedule_words(nb)

@@ -139,7 +139,9 @@ __global__ void __launch_bounds__(kWindow) group_kernel(ScheduleArgs a) {
 }
 
 // Iteration lists: for each (head, query tile) the ascending KV blocks kept by any of the tile's router
-// blocks, each tagged with which of them keep it (bit s = slot s of the tile).
+// blocks, and beside them, in an array of their own, which of those keep each one (bit s = slot s of the
+// tile).  A list entry is a plain tile index below nb, so the attention kernel forms its copy address
+// from it without masking any field off.
 __global__ void __launch_bounds__(256) compact_kernel(ScheduleArgs a) {
   __shared__ int wave_tot[4];
   __shared__ int slot_row[32];
@@ -149,6 +151,7 @@ __global__ void __launch_bounds__(256) compact_kernel(ScheduleArgs a) {
   if (threadIdx.x < a.group) slot_row[threadIdx.x] = a.perm[(size_t)tile * a.group + threadIdx.x];
   __syncthreads();
   int* out = a.list + (size_t)tile * a.nb;
+  unsigned char* fout = a.list_flags + (size_t)tile * a.nb;
   int base = 0;
   for (int j0 = 0; j0 < a.nb; j0 += 256) {
     const int j = j0 + threadIdx.x;
@@ -164,7 +167,10 @@ __global__ void __launch_bounds__(256) compact_kernel(ScheduleArgs a) {
     __syncthreads();
     int off = base;
     for (int w = 0; w < wave; ++w) off += wave_tot[w];
-    if (flags) out[off + before] = j | (flags << 24);
+    if (flags) {
+      out[off + before] = j;
+      fout[off + before] = (unsigned char)flags;
+    }
     base += wave_tot[0] + wave_tot[1] + wave_tot[2] + wave_tot[3];
     __syncthreads();
   }

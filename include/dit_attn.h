@@ -37,8 +37,13 @@
  *    synchronised, printed or thrown across the ABI.
  *  - Arguments are validated on the host before anything is queued; on error
  *    no work is queued and dit_attn_last_error() describes the problem.
- *  - q, k, v, o, mask and workspace must not overlap.  Calls that share a
- *    workspace must be ordered on one stream.
+ *  - Every buffer a call writes (o, route's mask, the workspace) must not
+ *    overlap any other buffer of the call (DIT_ERR_INVALID_ARG, checked on the
+ *    host over the bytes the call reads or writes); read-only inputs (q, k, v,
+ *    weights, positions, block_sparse's mask) may share memory with each other.
+ *    Calls that share a workspace must be ordered on one stream.
+ *  - Nothing is thrown across the ABI: a host-side failure (out of host memory
+ *    for the RoPE table) returns DIT_ERR_HOST.
  */
 #ifndef DIT_ATTN_H
 #define DIT_ATTN_H
@@ -54,15 +59,18 @@ typedef enum {
   DIT_ERR_INVALID_ARG = 1, /* null pointer, bad size, non-finite theta/eps, sparsity outside [0,1) */
   DIT_ERR_UNSUPPORTED = 2, /* head_dim not 96/128, block != 128, grid too large for one call  */
   DIT_ERR_WORKSPACE = 3,   /* workspace missing or smaller than dit_attn_workspace_bytes()    */
-  DIT_ERR_HIP = 4          /* a HIP runtime call failed; the HIP error string is in last_error */
+  DIT_ERR_HIP = 4,         /* a HIP runtime call failed; the HIP error string is in last_error */
+  DIT_ERR_HOST = 5         /* host-side failure (out of host memory); nothing was queued       */
 } dit_status;
 
 /* Bytes of device workspace that dense, route and block_sparse need for this
  * shape (enough for any of the three; about 2 * N * heads * head_dim * 2 bytes
  * for the K^/V fragment images plus the router's or the block-sparse schedule's
- * share: iteration lists, grouping table and the mask packed to bits).
- * Returns 0 if the shape is invalid. */
-size_t dit_attn_workspace_bytes(int T, int H, int W, int heads, int head_dim, int block);
+ * share: iteration lists and their slot flags, grouping table and the mask
+ * packed to bits).  `sparsity` is the router's (checked to lie in [0, 1)); the
+ * size does not depend on it, since block_sparse accepts any mask.
+ * Returns 0 if the shape or the sparsity is invalid. */
+size_t dit_attn_workspace_bytes(int T, int H, int W, int heads, int head_dim, int block, float sparsity);
 
 /* Number of KV blocks each query block keeps at `sparsity`:
  * nb - floor(sparsity * nb + 1e-9), clamped to [1, nb], where nb = ceil(N / block).
@@ -136,6 +144,16 @@ dit_status dit_attn_joint(const void* q, const void* k, const void* v,
                           float rope_theta, float eps,
                           void* o,
                           void* workspace, size_t workspace_bytes, void* hip_stream);
+
+/* Diagnostic: the order in which the workgroups of the attention calls (dense,
+ * block_sparse, joint: the K^/V prepass and the attention kernel) take their
+ * work.  0, the default, is the tuned order; 1 reverses it.  Every workgroup
+ * writes outputs of its own and reads none another writes, so no result may
+ * depend on the order: tests compare both orders bit for bit, which catches
+ * races inside a workgroup (its LDS double buffer) that a change of timing
+ * exposes.  Process-wide; applies to calls queued after it returns.
+ * DIT_ERR_INVALID_ARG for any other value. */
+dit_status dit_attn_set_launch_order(int order);
 
 /* Text of the last error on the calling thread ("" if the last call succeeded).
  * Valid until the next call on the same thread. */

@@ -50,6 +50,7 @@ def test_keep_count_matches_golden(lib):
 
 def test_workspace_bytes(lib):
     n = dit.dit_attn_workspace_bytes(31, 48, 84, 56)
+    assert n == dit.dit_attn_workspace_bytes(31, 48, 84, 56, 96, 128, 0.75)   # covers any mask: no sparsity term
     N, nb = 124992, 977
     assert n >= 56 * nb * 48 * 1024 + 2 * 56 * nb * 96 * 4 + 56 * nb * nb * 4   # images + router: pooled, scores
     big = dit.dit_attn_workspace_bytes(1, 640, 820, 1)    # 4100 blocks: no score matrix
@@ -57,37 +58,52 @@ def test_workspace_bytes(lib):
     assert n >= 56 * -(-N // 512) * nb * 4                  # sparse: KV lists per 512-token query tile
     assert n >= 56 * nb * 48 * 1024 + 56 * -(-N // 512) * nb * 4   # K^/V fragment images + sparse lists
     nqt, words = -(-N // 512), -(-nb // 64)
-    sched = 56 * nqt * nb * 4 + 56 * nqt * 4 + 56 * nqt * 4 * 4 + 56 * nb * words * 8   # lists, counts, slots, bits
+    sched = (56 * nqt * nb * 4 + 56 * nqt * nb + 56 * nqt * 4 + 56 * nqt * 4 * 4   # lists, flags, counts, slots
+             + 56 * nb * words * 8)                                                  # packed mask rows
     assert n >= 56 * nb * 48 * 1024 + sched
     assert dit.dit_attn_workspace_bytes(31, 48, 84, 56, 64) == 0    # head_dim 64 unsupported
     n128 = dit.dit_attn_workspace_bytes(31, 48, 84, 42, 128)        # 42 heads x 128: 64 KB tile images
     assert n128 >= 42 * nb * 64 * 1024 + 2 * 42 * nb * 128 * 4 + 42 * nb * nb * 4
     assert dit.dit_attn_workspace_bytes(31, 48, 84, 56, 96, 64) == 0
     assert dit.dit_attn_workspace_bytes(0, 48, 84, 56) == 0
+    for bad in (1.0, -0.1, float("nan"), float("inf")):                 # sparsity outside [0, 1)
+        assert dit.dit_attn_workspace_bytes(31, 48, 84, 56, 96, 128, bad) == 0
 
 
-FAKE = 1 << 20   # an aligned non-null address; validation fails before anything dereferences it
+def test_workspace_bytes_signature_matches_header():
+    text = re.sub(r"/\*.*?\*/", "", open(HEADERS[0]).read(), flags=re.S)
+    decl = re.search(r"size_t\s+dit_attn_workspace_bytes\s*\(([^)]*)\)", text).group(1)
+    params = [p.split()[-1] for p in decl.split(",")]
+    assert params == ["T", "H", "W", "heads", "head_dim", "block", "sparsity"]
+    assert "float sparsity" in decl
+
+
+# Stand-in addresses, aligned, non-null and 16 MB apart (every buffer of these shapes fits in 16 MB, the
+# workspace bound the size checks use excepted); validation fails before anything dereferences them.
+FAKE = 1 << 24
+Q, K, V, WQ, WK, O, MASK, WS, QP, KP = ((i + 1) << 24 for i in range(10))
+WS = 1 << 40     # far above the others: the workspace bytes a call needs may exceed 16 MB
 
 
 def _dense(lib, **kw):
-    a = dict(q=FAKE, k=FAKE, v=FAKE, wq=FAKE, wk=FAKE, T=2, H=4, W=4, heads=2, d=96, theta=1e4, eps=1e-6,
-             o=FAKE, ws=FAKE, wsb=1 << 30, stream=None)
+    a = dict(q=Q, k=K, v=V, wq=WQ, wk=WK, T=2, H=4, W=4, heads=2, d=96, theta=1e4, eps=1e-6,
+             o=O, ws=WS, wsb=1 << 30, stream=None)
     a.update(kw)
     return lib.dit_attn_dense(a["q"], a["k"], a["v"], a["wq"], a["wk"], a["T"], a["H"], a["W"], a["heads"], a["d"],
                               a["theta"], a["eps"], a["o"], a["ws"], a["wsb"], a["stream"])
 
 
 def _route(lib, **kw):
-    a = dict(q=FAKE, k=FAKE, wq=FAKE, wk=FAKE, T=2, H=4, W=4, heads=2, d=96, theta=1e4, eps=1e-6, s=0.75,
-             block=128, mask=FAKE, ws=FAKE, wsb=1 << 30, stream=None)
+    a = dict(q=Q, k=K, wq=WQ, wk=WK, T=2, H=4, W=4, heads=2, d=96, theta=1e4, eps=1e-6, s=0.75,
+             block=128, mask=MASK, ws=WS, wsb=1 << 30, stream=None)
     a.update(kw)
     return lib.dit_attn_route(a["q"], a["k"], a["wq"], a["wk"], a["T"], a["H"], a["W"], a["heads"], a["d"],
                               a["theta"], a["eps"], a["s"], a["block"], a["mask"], a["ws"], a["wsb"], a["stream"])
 
 
 def _sparse(lib, **kw):
-    a = dict(q=FAKE, k=FAKE, v=FAKE, wq=FAKE, wk=FAKE, T=2, H=4, W=4, heads=2, d=96, theta=1e4, eps=1e-6,
-             block=128, mask=FAKE, o=FAKE, ws=FAKE, wsb=1 << 30, stream=None)
+    a = dict(q=Q, k=K, v=V, wq=WQ, wk=WK, T=2, H=4, W=4, heads=2, d=96, theta=1e4, eps=1e-6,
+             block=128, mask=MASK, o=O, ws=WS, wsb=1 << 30, stream=None)
     a.update(kw)
     return lib.dit_attn_block_sparse(a["q"], a["k"], a["v"], a["wq"], a["wk"], a["T"], a["H"], a["W"], a["heads"],
                                      a["d"], a["theta"], a["eps"], a["block"], a["mask"], a["o"], a["ws"], a["wsb"],
@@ -99,7 +115,7 @@ def _sparse(lib, **kw):
     (dict(q=None), B.DIT_ERR_INVALID_ARG, "null"),
     (dict(k=None), B.DIT_ERR_INVALID_ARG, "null"),
     (dict(wq=None), B.DIT_ERR_INVALID_ARG, "null"),
-    (dict(q=FAKE + 2), B.DIT_ERR_INVALID_ARG, "aligned"),
+    (dict(q=Q + 2), B.DIT_ERR_INVALID_ARG, "aligned"),
     (dict(T=0), B.DIT_ERR_INVALID_ARG, "grid"),
     (dict(heads=-1), B.DIT_ERR_INVALID_ARG, "grid"),
     (dict(d=64), B.DIT_ERR_UNSUPPORTED, "head_dim"),
@@ -111,7 +127,7 @@ def _sparse(lib, **kw):
     (dict(eps=float("nan")), B.DIT_ERR_INVALID_ARG, "eps"),
     (dict(ws=None), B.DIT_ERR_WORKSPACE, "workspace"),
     (dict(wsb=100), B.DIT_ERR_WORKSPACE, "need"),
-    (dict(ws=FAKE + 16), B.DIT_ERR_INVALID_ARG, "256-byte"),
+    (dict(ws=WS + 16), B.DIT_ERR_INVALID_ARG, "256-byte"),
 ])
 def test_validation_errors(lib, call, kw, status, text):
     assert call(lib, **kw) == status
@@ -158,8 +174,8 @@ def test_missing_library_fails_loudly(tmp_path):
 
 
 def _joint(lib, **kw):
-    a = dict(q=FAKE, k=FAKE, v=FAKE, wq=FAKE, wk=FAKE, qp=FAKE, kp=FAKE, nq=20, nk=50, heads=2, d=96, maxp=16,
-             theta=1e4, eps=1e-6, o=FAKE, ws=FAKE, wsb=1 << 30, stream=None)
+    a = dict(q=Q, k=K, v=V, wq=WQ, wk=WK, qp=QP, kp=KP, nq=20, nk=50, heads=2, d=96, maxp=16,
+             theta=1e4, eps=1e-6, o=O, ws=WS, wsb=1 << 30, stream=None)
     a.update(kw)
     return lib.dit_attn_joint(a["q"], a["k"], a["v"], a["wq"], a["wk"], a["qp"], a["kp"], a["nq"], a["nk"], a["heads"],
                               a["d"], a["maxp"], a["theta"], a["eps"], a["o"], a["ws"], a["wsb"], a["stream"])
@@ -170,8 +186,8 @@ def _joint(lib, **kw):
     (dict(kp=None), B.DIT_ERR_INVALID_ARG, "null"),
     (dict(v=None), B.DIT_ERR_INVALID_ARG, "null"),
     (dict(q=None), B.DIT_ERR_INVALID_ARG, "null"),
-    (dict(qp=FAKE + 2), B.DIT_ERR_INVALID_ARG, "4-byte"),
-    (dict(v=FAKE + 8), B.DIT_ERR_INVALID_ARG, "aligned"),
+    (dict(qp=QP + 2), B.DIT_ERR_INVALID_ARG, "4-byte"),
+    (dict(v=V + 8), B.DIT_ERR_INVALID_ARG, "aligned"),
     (dict(nq=0), B.DIT_ERR_INVALID_ARG, "token counts"),
     (dict(nk=-3), B.DIT_ERR_INVALID_ARG, "token counts"),
     (dict(maxp=0), B.DIT_ERR_INVALID_ARG, "max_pos"),
@@ -182,11 +198,62 @@ def _joint(lib, **kw):
     (dict(theta=-1.0), B.DIT_ERR_INVALID_ARG, "rope_theta"),
     (dict(ws=None), B.DIT_ERR_WORKSPACE, "workspace"),
     (dict(wsb=64), B.DIT_ERR_WORKSPACE, "need"),
-    (dict(ws=FAKE + 128), B.DIT_ERR_INVALID_ARG, "256-byte"),
+    (dict(ws=WS + 128), B.DIT_ERR_INVALID_ARG, "256-byte"),
 ])
 def test_joint_validation_errors(lib, kw, status, text):
     assert _joint(lib, **kw) == status
     assert text in B.dit_attn_last_error()
+
+
+# Buffers a call writes may not overlap any other buffer of the call; read-only inputs may alias.
+@pytest.mark.parametrize("call,kw,text", [
+    (_dense, dict(o=Q), "q overlaps o"),
+    (_dense, dict(o=V + 4096), "v overlaps o"),                 # partial overlap (o starts inside v)
+    (_dense, dict(o=WK), "wk overlaps o"),
+    (_dense, dict(ws=(K // 256) * 256), "k overlaps workspace"),
+    (_dense, dict(o=WS + (1 << 16)), "o overlaps workspace"),
+    (_route, dict(mask=K + 256), "k overlaps mask"),
+    (_route, dict(ws=WQ - 4096), "wq overlaps workspace"),
+    (_sparse, dict(o=MASK), "mask overlaps o"),
+    (_sparse, dict(ws=MASK - 256), "mask overlaps workspace"),
+    (_joint, dict(o=KP), "k_pos overlaps o"),
+    (_joint, dict(ws=QP), "q_pos overlaps workspace"),
+])
+def test_written_buffers_must_not_overlap(lib, call, kw, text):
+    assert call(lib, **kw) == B.DIT_ERR_INVALID_ARG
+    assert text in B.dit_attn_last_error()
+
+
+NO_THROW_PROBE = r'''
+import ctypes, resource, sys
+sys.path.insert(0, ROOT)
+from image_diffusion_transformer_amd import _binding as B
+lib = B.load_library()
+vm = int(open("/proc/self/status").read().split("VmSize:")[1].split()[0]) * 1024
+# 128 MB of address space beyond what the process holds: the RoPE table of a joint call at head dim 128
+# with 2^20 positions per axis (3 x 2^20 rows x 44 floats = 554 MB) cannot be allocated.
+resource.setrlimit(resource.RLIMIT_AS, (vm + (128 << 20), resource.RLIM_INFINITY))
+big = (1 << 40)
+st = lib.dit_attn_joint(1 << 24, 2 << 24, 3 << 24, 4 << 24, 5 << 24, 6 << 24, 7 << 24, 20, 50, 2, 128, 1 << 20,
+                        1e4, 1e-6, 8 << 24, big, 1 << 36, None)
+print(st, B.dit_attn_last_error())
+'''
+
+
+@pytest.mark.skipif(os.path.exists("/dev/kfd"), reason="a GPU is present: were the address-space limit to fail to "
+                    "take, the call would go on to a device copy to a stand-in address")
+def test_host_allocation_failure_returns_status_not_exception():
+    """A host allocation failure inside an entry point (the RoPE table) comes back as DIT_ERR_HOST with a message:
+    no C++ exception crosses the C ABI (it would terminate the process)."""
+    import subprocess
+    import sys
+    root = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+    code = f"ROOT = {root!r}\n" + NO_THROW_PROBE
+    r = subprocess.run([sys.executable, "-c", code], capture_output=True, text=True, timeout=120)
+    assert r.returncode == 0, r.stderr[-2000:]
+    status, _, msg = r.stdout.strip().partition(" ")
+    assert int(status) == B.DIT_ERR_HOST, r.stdout
+    assert "host memory" in msg
 
 
 def test_joint_workspace_bytes(lib):
@@ -260,3 +327,13 @@ def test_product_package_never_imports_the_oracle():
             "assert not bad, bad")
     r = subprocess.run([sys.executable, "-c", code], cwd=root, capture_output=True, text=True, timeout=120)
     assert r.returncode == 0, r.stderr[-2000:]
+
+
+def test_launch_order_values(lib):
+    """The diagnostic workgroup order takes 0 or 1 only (host-side; no device is touched)."""
+    assert lib.dit_attn_set_launch_order(2) == B.DIT_ERR_INVALID_ARG
+    assert "launch order" in B.dit_attn_last_error()
+    assert lib.dit_attn_set_launch_order(-1) == B.DIT_ERR_INVALID_ARG
+    assert lib.dit_attn_set_launch_order(1) == B.DIT_OK
+    assert lib.dit_attn_set_launch_order(0) == B.DIT_OK
+    assert B.dit_attn_last_error() == ""

@@ -1,0 +1,224 @@
+"""Out-of-bounds and race checks of every attention entry point, through the C ABI.
+
+* Guard bands: O, the mask and the workspace sit between two 4 KB bands of sentinel bytes, on grids whose last
+  router block is ragged (N mod 128 = 64 or 72), at both head dims.  After each call every band byte must be
+  intact, every O element written (O starts as bf16 NaN) and every mask byte 0 or 1 (it starts as 0xA5).
+* Determinism: each entry point, under both softmax kernels (static shift and running maximum), gives the same
+  bits on a repeated call, with the workgroups taking their work in reversed order, and while another stream
+  keeps part of the GPU busy.  No workgroup reads what another writes, so none of these may change a bit; a
+  race inside a workgroup (its LDS double buffer) would show up as a difference.
+* Temporaries the binding allocates for a call on a side stream belong to that stream, so allocations on the
+  current stream right after the call cannot take their memory while the call's kernels still run.
+"""
+import numpy as np
+import pytest
+import torch
+
+import image_diffusion_transformer_amd as dit
+from oracle import attention as A
+from oracle import router as R
+from synth import custom_workload, make_inputs
+
+pytestmark = pytest.mark.gpu
+DEV = torch.device("cuda:0")
+MAX_ABS, REL_L2 = 2e-2, 1e-2
+GUARD = 4096          # bytes of sentinel on each side of a buffer (keeps the payload 256-byte aligned)
+SENT = 0xA5
+
+
+def t16(b):
+    return torch.from_numpy(b.bits.view(np.int16)).to(DEV).view(torch.bfloat16)
+
+
+def upload(x):
+    return (t16(x.q), t16(x.k), t16(x.v), torch.from_numpy(x.wq).to(DEV), torch.from_numpy(x.wk).to(DEV))
+
+
+def banded(nbytes, fill):
+    """A uint8 device buffer [GUARD sentinel | nbytes of `fill` | GUARD sentinel] and its middle part."""
+    buf = torch.full((GUARD + nbytes + GUARD,), SENT, dtype=torch.uint8, device=DEV)
+    mid = buf[GUARD:GUARD + nbytes]
+    mid.fill_(fill)
+    return buf, mid
+
+
+def bands_intact(buf, nbytes, what):
+    torch.cuda.synchronize()
+    head, tail = buf[:GUARD], buf[GUARD + nbytes:]
+    bad_head = int((head != SENT).sum())
+    bad_tail = int((tail != SENT).sum())
+    assert bad_head == 0 and bad_tail == 0, f"{what}: {bad_head} bytes before and {bad_tail} after were written"
+
+
+def check_close(got, ref, what):
+    err = np.abs(got.astype(np.float64) - ref)
+    rel = float(np.linalg.norm(err) / max(np.linalg.norm(ref), 1e-30))
+    print(f"{what}: max_abs={err.max():.3e} rel_l2={rel:.3e}", flush=True)
+    assert np.all(np.isfinite(got)) and err.max() <= MAX_ABS and rel <= REL_L2, (what, err.max(), rel)
+
+
+# grids with a ragged last block: N = 192, 960 (N mod 128 = 64); 200, 1352 (72)
+RAGGED = [(1, 8, 24), (4, 12, 20), (2, 10, 10), (2, 26, 26)]
+
+
+@pytest.mark.parametrize("d", [96, 128])
+@pytest.mark.parametrize("grid", RAGGED, ids=lambda g: "x".join(map(str, g)))
+def test_guard_bands_dense_route_sparse(grid, d):
+    T, H, W = grid
+    heads = 3 if d == 96 else 2
+    wl = custom_workload(T, H, W, heads, seed=70 + T * H * W % 97, head_dim=d)
+    N, nb = wl.N, wl.nb
+    print(f"case guard N={N} (mod 128 = {N % 128}) heads={heads} d={d}", flush=True)
+    x = make_inputs(wl)
+    q, k, v, wq, wk = upload(x)
+    nbytes_o = N * heads * d * 2
+    nbytes_m = heads * nb * nb
+    nbytes_ws = dit.dit_attn_workspace_bytes(T, H, W, heads, d, 128, 0.75)
+    ws_buf, ws = banded(nbytes_ws, 0x5A)
+    # dense
+    o_buf, o_mid = banded(nbytes_o, 0xFF)                  # 0xFFFF is a bf16 NaN: every element must be written
+    o = o_mid.view(torch.bfloat16).view(N, heads, d)
+    dit.dit_attn_dense(q, k, v, wq, wk, grid, wl.theta, wl.eps, o=o, workspace=ws)
+    bands_intact(o_buf, nbytes_o, "dense O")
+    bands_intact(ws_buf, nbytes_ws, "dense workspace")
+    assert not bool(torch.isnan(o).any()), "dense: some O elements were not written"
+    # route
+    m_buf, m_mid = banded(nbytes_m, SENT)
+    mask = m_mid.view(heads, nb, nb)
+    dit.dit_attn_route(q, k, wq, wk, grid, 0.75, wl.theta, wl.eps, mask=mask, workspace=ws)
+    bands_intact(m_buf, nbytes_m, "route mask")
+    bands_intact(ws_buf, nbytes_ws, "route workspace")
+    assert bool(((mask == 0) | (mask == 1)).all()), "route: some mask bytes were not written"
+    mref = R.route_mask(x.q, x.k, x.wq, x.wk, T, H, W, 0.75, theta=wl.theta, eps=wl.eps)
+    assert np.array_equal(mask.cpu().numpy(), mref), "route mask differs from the oracle"
+    # block-sparse on that mask
+    o2_buf, o2_mid = banded(nbytes_o, 0xFF)
+    o2 = o2_mid.view(torch.bfloat16).view(N, heads, d)
+    dit.dit_attn_block_sparse(q, k, v, wq, wk, grid, mask, wl.theta, wl.eps, o=o2, workspace=ws)
+    bands_intact(o2_buf, nbytes_o, "block-sparse O")
+    bands_intact(ws_buf, nbytes_ws, "block-sparse workspace")
+    bands_intact(m_buf, nbytes_m, "block-sparse mask (input)")
+    assert not bool(torch.isnan(o2).any()), "block-sparse: some O elements were not written"
+    ref = A.attention(x.q, x.k, x.v, x.wq, x.wk, T, H, W, wl.theta, wl.eps, mask=mref)
+    check_close(o2.float().cpu().numpy(), ref, f"block-sparse {grid} d={d}")
+
+
+@pytest.mark.parametrize("d", [96, 128])
+@pytest.mark.parametrize("grid", [(1, 8, 24), (2, 10, 10)], ids=lambda g: "x".join(map(str, g)))
+def test_guard_bands_joint(grid, d):
+    """Joint call with the last N - 40 grid tokens as queries against all N as keys (both counts ragged)."""
+    T, H, W = grid
+    heads = 2
+    wl = custom_workload(T, H, W, heads, seed=90 + T, head_dim=d)
+    N = wl.N
+    nq = N - 40
+    x = make_inputs(wl)
+    q, k, v, wq, wk = upload(x)
+    tt, hh, ww = np.meshgrid(np.arange(T), np.arange(H), np.arange(W), indexing="ij")
+    pos = np.stack([tt.ravel(), hh.ravel(), ww.ravel()], axis=1).astype(np.int32)
+    max_pos = int(pos.max()) + 1
+    qs = q[N - nq:].contiguous()
+    nbytes_o = nq * heads * d * 2
+    nbytes_ws = dit.dit_attn_joint_workspace_bytes(nq, N, heads, d, max_pos)
+    ws_buf, ws = banded(nbytes_ws, 0x5A)
+    o_buf, o_mid = banded(nbytes_o, 0xFF)
+    o = o_mid.view(torch.bfloat16).view(nq, heads, d)
+    qp = torch.from_numpy(np.ascontiguousarray(pos[N - nq:])).to(DEV)
+    kp = torch.from_numpy(pos).to(DEV)
+    print(f"case guard joint nq={nq} nk={N} d={d}", flush=True)
+    dit.dit_attn_joint(qs, k, v, wq, wk, qp, kp, max_pos, wl.theta, wl.eps, o=o, workspace=ws)
+    bands_intact(o_buf, nbytes_o, "joint O")
+    bands_intact(ws_buf, nbytes_ws, "joint workspace")
+    assert not bool(torch.isnan(o).any()), "joint: some O elements were not written"
+    ref = A.attention(x.q, x.k, x.v, x.wq, x.wk, T, H, W, wl.theta, wl.eps)[N - nq:]
+    check_close(o.float().cpu().numpy(), ref, f"joint {grid} d={d}")
+
+
+def busy_side_stream():
+    """Keeps a side stream (default priority) busy with fp32 matrix products while the calls under test run."""
+    s = torch.cuda.Stream()
+    with torch.cuda.stream(s):
+        a = torch.randn(4096, 4096, device=DEV)
+        for _ in range(24):
+            a = torch.mm(a, a).clamp_(-1.0, 1.0)
+    return s
+
+
+def run_all(x, grid, sparsity, ws, order=0, perturb=False):
+    """Every entry point once: dense, route, block-sparse on the route's mask, joint over the grid tokens."""
+    wl = x.workload
+    q, k, v, wq, wk = upload(x)
+    N, heads, d = wl.N, wl.heads, wl.head_dim
+    tt, hh, ww = np.meshgrid(*(np.arange(n) for n in grid), indexing="ij")
+    pos = torch.from_numpy(np.stack([tt.ravel(), hh.ravel(), ww.ravel()], axis=1).astype(np.int32)).to(DEV)
+    torch.cuda.synchronize()
+    side = busy_side_stream() if perturb else None
+    dit.dit_attn_set_launch_order(order)
+    try:
+        od = dit.dit_attn_dense(q, k, v, wq, wk, grid, wl.theta, wl.eps, workspace=ws)
+        m = dit.dit_attn_route(q, k, wq, wk, grid, sparsity, wl.theta, wl.eps, workspace=ws)
+        osp = dit.dit_attn_block_sparse(q, k, v, wq, wk, grid, m, wl.theta, wl.eps, workspace=ws)
+        oj = dit.dit_attn_joint(q, k, v, wq, wk, pos, pos, max(grid), wl.theta, wl.eps)
+    finally:
+        dit.dit_attn_set_launch_order(0)
+    torch.cuda.synchronize()
+    if side is not None:
+        side.synchronize()
+    return [t.view(torch.uint8).cpu().numpy() if t.dtype != torch.uint8 else t.cpu().numpy()
+            for t in (od, m, osp, oj)]
+
+
+@pytest.mark.parametrize("scale", [1.0, 1.75], ids=["static", "online"])
+@pytest.mark.parametrize("d", [96, 128])
+def test_bitwise_determinism_repeat_reversed_and_loaded(scale, d):
+    # 6x24x40 = 5760 tokens (45 router blocks, ragged 0), 4 heads at 96 / 3 at 128: 12-45 query tiles per head
+    heads = 4 if d == 96 else 3
+    wl = custom_workload(6, 24, 40, heads, seed=81, head_dim=d, weight_scale=scale)
+    grid = (wl.T, wl.H, wl.W)
+    x = make_inputs(wl)
+    print(f"case determinism d={d} weights x{scale} N={wl.N}", flush=True)
+    ws = torch.empty(dit.dit_attn_workspace_bytes(*grid, heads, d, 128, 0.75), dtype=torch.uint8, device=DEV)
+    names = ["dense O", "route mask", "block-sparse O", "joint O"]
+    base = run_all(x, grid, 0.75, ws)
+    for label, kw in [("repeat", {}), ("reversed order", {"order": 1}), ("loaded GPU", {"perturb": True}),
+                      ("reversed + loaded", {"order": 1, "perturb": True})]:
+        got = run_all(x, grid, 0.75, ws, **kw)
+        for n, a, b in zip(names, base, got):
+            assert np.array_equal(a, b), f"{n} differs bitwise ({label})"
+    # and the results are right (the dense O against the oracle on every row)
+    o = base[0].view(np.uint16).view(np.int16)
+    o = torch.from_numpy(o).view(torch.bfloat16).float().numpy().reshape(wl.N, heads, d)
+    check_close(o, A.attention(x.q, x.k, x.v, x.wq, x.wk, *grid, wl.theta, wl.eps), f"dense d={d} x{scale}")
+
+
+def test_launch_order_rejects_other_values():
+    with pytest.raises(dit.DitAttnError):
+        dit.dit_attn_set_launch_order(2)
+    dit.dit_attn_set_launch_order(0)
+
+
+def test_side_stream_temporaries_survive_allocation_churn():
+    """Calls on a busy side stream, with o, mask and workspace allocated by the binding; right after, the current
+    stream allocates blocks of the same sizes and overwrites them.  Had the temporaries been taken on the current
+    stream, these would reuse their memory before the side stream's kernels ran."""
+    x = make_inputs("s4")
+    wl = x.workload
+    grid = (wl.T, wl.H, wl.W)
+    q, k, v, wq, wk = upload(x)
+    torch.cuda.synchronize()
+    side = busy_side_stream()
+    od = dit.dit_attn_dense(q, k, v, wq, wk, grid, wl.theta, wl.eps, stream=side)
+    m = dit.dit_attn_route(q, k, wq, wk, grid, 0.75, wl.theta, wl.eps, stream=side)
+    osp = dit.dit_attn_block_sparse(q, k, v, wq, wk, grid, m, wl.theta, wl.eps, stream=side)
+    sizes = [dit.dit_attn_workspace_bytes(*grid, wl.heads, wl.head_dim, 128, 0.75), od.numel() * 2, m.numel()]
+    junk = [torch.full((n,), 0x7F, dtype=torch.uint8, device=DEV) for n in sizes for _ in range(4)]
+    del junk
+    side.synchronize()
+    torch.cuda.synchronize()
+    check_close(od.float().cpu().numpy(), A.attention(x.q, x.k, x.v, x.wq, x.wk, *grid, wl.theta, wl.eps),
+                "dense on a side stream")
+    mref = R.route_mask(x.q, x.k, x.wq, x.wk, *grid, 0.75, theta=wl.theta, eps=wl.eps)
+    assert np.array_equal(m.cpu().numpy(), mref), "route mask on a side stream differs from the oracle"
+    check_close(osp.float().cpu().numpy(),
+                A.attention(x.q, x.k, x.v, x.wq, x.wk, *grid, wl.theta, wl.eps, mask=mref),
+                "block-sparse on a side stream")
