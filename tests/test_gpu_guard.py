@@ -168,7 +168,10 @@ def run_all(x, grid, sparsity, ws, order=0, perturb=False):
             for t in (od, m, osp, oj)]
 
 
-@pytest.mark.parametrize("scale", [1.0, 1.75], ids=["static", "online"])
+# 1.5 times the norm weights puts the pairwise logit bound past the static shift's range (the running-maximum
+# kernel runs) while keeping the largest logits near 11, where rounding q^ and k^ to bf16 leaves O about 1e-2 from
+# the oracle at most (modelled on the CPU); at 1.75 times (logits near 16) it measured 2.4e-2 on these tensors.
+@pytest.mark.parametrize("scale", [1.0, 1.5], ids=["static", "online"])
 @pytest.mark.parametrize("d", [96, 128])
 def test_bitwise_determinism_repeat_reversed_and_loaded(scale, d):
     # 6x24x40 = 5760 tokens (45 router blocks, ragged 0), 4 heads at 96 / 3 at 128: 12-45 query tiles per head
