@@ -23,7 +23,8 @@ STATUS_NAMES = {0: "DIT_OK", 1: "DIT_ERR_INVALID_ARG", 2: "DIT_ERR_UNSUPPORTED",
                 3: "DIT_ERR_WORKSPACE", 4: "DIT_ERR_HIP", 5: "DIT_ERR_HOST"}
 
 EXPORTS = ("dit_attn_workspace_bytes", "dit_attn_keep_count", "dit_attn_dense", "dit_attn_route",
-           "dit_attn_block_sparse", "dit_attn_joint_workspace_bytes", "dit_attn_joint", "dit_attn_set_launch_order",
+           "dit_attn_block_sparse", "dit_attn_joint_workspace_bytes", "dit_attn_joint", "dit_attn_dense_noalloc",
+           "dit_attn_set_launch_order",
            "dit_attn_last_error", "dit_adaln_modulate", "dit_gated_residual", "dit_swiglu")
 
 _lib = None
@@ -67,6 +68,8 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
         lib.dit_gated_residual.restype = i
         lib.dit_swiglu.argtypes = [vp, ll, i, vp, vp]
         lib.dit_swiglu.restype = i
+        lib.dit_attn_dense_noalloc.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, i, f, f, vp, vp]
+        lib.dit_attn_dense_noalloc.restype = i
         lib.dit_attn_set_launch_order.argtypes = [i]
         lib.dit_attn_set_launch_order.restype = i
         lib.dit_attn_last_error.argtypes = []
@@ -318,6 +321,25 @@ def dit_swiglu(gate_up, out=None, stream=None):
     _on(gate_up.device, gate_up=gate_up, out=out)
     _check(load_library().dit_swiglu(_ptr(gate_up), tokens, ffn, _ptr(out), _stream(stream)))
     return out
+
+
+NOALLOC_SCRATCH_BYTES = 64 << 20
+
+
+def dit_attn_dense_noalloc(q, k, v, wq, wk, grid, rope_theta=10000.0, eps=1e-6, o=None, stream=None):
+    """dit_attn_dense without a workspace: its scratch is the library's static 64 MiB per-GPU array, so the C call
+    allocates no device memory (pass ``o`` too and nothing is allocated at all).  Calls that overlap in time on
+    one GPU race on that scratch."""
+    T, H, W, heads, d = _shape(q, grid)
+    _attn_operands(q, k, v, wq, wk, T * H * W, heads, d)
+    if o is None:
+        with _on_stream(stream):
+            o = torch.empty_like(q)
+    _dev(o, "o", torch.bfloat16, tuple(q.shape))
+    _on(q.device, q=q, k=k, v=v, wq=wq, wk=wk, o=o)
+    _check(load_library().dit_attn_dense_noalloc(_ptr(q), _ptr(k), _ptr(v), _ptr(wq), _ptr(wk), T, H, W, heads, d,
+                                                  rope_theta, eps, _ptr(o), _stream(stream)))
+    return o
 
 
 def dit_attn_set_launch_order(order: int) -> None:

@@ -564,6 +564,91 @@ dit_status dit_attn_joint(const void* q, const void* k, const void* v, const flo
 }  // extern "C"
 
 // ------------------------------------------------------------------------------------------------
+// Allocation-free dense attention (dit_attn_dense_noalloc): the RoPE table and the K^/V fragment images
+// live in `scratch`, a static device array of the library, instead of a caller's workspace.
+
+namespace {
+
+constexpr size_t kStaticScratchBytes = DIT_ATTN_NOALLOC_SCRATCH_BYTES;   // 64 MiB per GPU, held until exit
+static_assert(kStaticScratchBytes == (64ull << 20), "static scratch size");
+
+// The array's name is a host-side stand-in in host code: only the address hipGetSymbolAddress returns (per
+// device) is handed to kernels or copies.
+static __device__ __align__(256) unsigned char scratch[kStaticScratchBytes];
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+// Device address of this device's `scratch`, looked up once per device with that device current.
+dit_status static_scratch(int dev, void** out) {
+  if (dev < 0 || dev >= kMaxDevices) return fail(DIT_ERR_UNSUPPORTED, "device %d is beyond %d", dev, kMaxDevices);
+  std::lock_guard<std::mutex> lk(g_scratch_mu);
+  if (g_scratch_ptr[dev] == nullptr) {
+    void* p = nullptr;
+    const hipError_t e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return fail_hip(e, "hipGetSymbolAddress(scratch)");
+    if (p == nullptr) return fail(DIT_ERR_HIP, "hipGetSymbolAddress(scratch) returned a null address");
+    g_scratch_ptr[dev] = p;
+  }
+  *out = g_scratch_ptr[dev];
+  return DIT_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+dit_status dit_attn_dense_noalloc(const void* q, const void* k, const void* v, const float* wq, const float* wk,
+                                  int T, int H, int W, int heads, int head_dim, float rope_theta, float eps, void* o,
+                                  void* hip_stream) {
+  clear_error();
+  return guarded([&]() -> dit_status {
+    Shape s;
+    dit_status st = check_shape(T, H, W, heads, head_dim, s);
+    if (st != DIT_OK) return st;
+    if ((st = check_common(q, k, wq, wk, rope_theta, eps)) != DIT_OK) return st;
+    if (!v || !o) return fail(DIT_ERR_INVALID_ARG, "null v or o");
+    if (!aligned16(v) || !aligned16(o)) return fail(DIT_ERR_INVALID_ARG, "v and o must be 16-byte aligned");
+    // The dense part of the workspace layout: RoPE table, then the fragment images.
+    const Layout L = make_layout(s);
+    const size_t need = L.kvf + (size_t)s.heads * s.nb * dit::tile_image_bytes(s.d);
+    if (need > kStaticScratchBytes)
+      return fail(DIT_ERR_UNSUPPORTED,
+                  "needs %zu bytes of scratch (heads x ceil(N/128) tiles of %zu bytes plus the RoPE table); the "
+                  "static scratch holds %zu: use dit_attn_dense with a workspace",
+                  need, dit::tile_image_bytes(s.d), kStaticScratchBytes);
+    hipStream_t stream = (hipStream_t)hip_stream;
+    int dev = -1;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return fail_hip(e, "hipGetDevice");
+    if (stream != nullptr) {
+      int sdev = -1;
+      e = hipStreamGetDevice(stream, &sdev);
+      if (e != hipSuccess) return fail_hip(e, "hipStreamGetDevice");
+      if (sdev != dev)
+        return fail(DIT_ERR_INVALID_ARG, "the stream belongs to device %d but device %d is current", sdev, dev);
+    }
+    void* ws = nullptr;
+    if ((st = static_scratch(dev, &ws)) != DIT_OK) return st;
+    const size_t tb = (size_t)s.N * s.heads * s.d * 2, wb = (size_t)s.d * 4;
+    const Buf bufs[] = {{q, tb, "q", false},   {k, tb, "k", false},   {v, tb, "v", false},
+                        {wq, wb, "wq", false},  {wk, wb, "wk", false}, {o, tb, "o", true},
+                        {ws, need, "the static scratch", true}};
+    if ((st = check_disjoint(bufs)) != DIT_OK) return st;
+    // Nothing in the scratch needs to start at zero: the table is uploaded and every fragment-image byte
+    // of the call's tiles is written by the prepass before the attention kernel reads it.
+    if ((st = upload_table(s, rope_theta, ws, L, stream)) != DIT_OK) return st;
+    const dit::AttnArgs a = attn_args(s, q, k, v, wq, wk, eps, o, ws, L);
+    e = dit::launch_attn_dense(a, stream);
+    if (e != hipSuccess) return fail_hip(e, "attention kernel launch");
+    return DIT_OK;
+  });
+}
+
+}  // extern "C"
+
+// ------------------------------------------------------------------------------------------------
 // Operators around attention (dit_block.h)
 
 namespace {

@@ -145,6 +145,31 @@ dit_status dit_attn_joint(const void* q, const void* k, const void* v,
                           void* o,
                           void* workspace, size_t workspace_bytes, void* hip_stream);
 
+/* Dense attention for callers that cannot allocate device memory (code under
+ * HIP graph capture, tight serving loops, harnesses that forbid hipMalloc):
+ * dit_attn_dense without a workspace.  Its scratch (the RoPE table and the
+ * K^/V fragment images) is a static device array of the library, one per GPU,
+ * of DIT_ATTN_NOALLOC_SCRATCH_BYTES (64 MiB), held from the call that first
+ * uses it on a GPU until the process ends.  The call allocates no device
+ * memory and calls no allocating routine.
+ *  - Arguments, layouts and results as dit_attn_dense (the same kernels: the
+ *    output equals dit_attn_dense's bit for bit).
+ *  - Size limit: the RoPE table plus heads * ceil(N / 128) tile images
+ *    (48 KiB each at head_dim 96, 64 KiB at 128) must fit the scratch; larger
+ *    calls return DIT_ERR_UNSUPPORTED (at head_dim 96 about 1,360 tiles, e.g.
+ *    56 heads x 3,072 tokens or 8 heads x 21,760 tokens).
+ *  - The current device must be the stream's device (DIT_ERR_INVALID_ARG).
+ *  - All calls on one GPU share its scratch and it keeps the last call's
+ *    contents (nothing in it needs to start at zero): calls that overlap in
+ *    time on one GPU (different streams without ordering) race and give wrong
+ *    results.  Order them on one stream. */
+#define DIT_ATTN_NOALLOC_SCRATCH_BYTES ((size_t)64 << 20)
+dit_status dit_attn_dense_noalloc(const void* q, const void* k, const void* v,
+                                  const float* wq, const float* wk,
+                                  int T, int H, int W, int heads, int head_dim,
+                                  float rope_theta, float eps,
+                                  void* o, void* hip_stream);
+
 /* Diagnostic: the order in which the workgroups of the attention calls (dense,
  * block_sparse, joint: the K^/V prepass and the attention kernel) take their
  * work.  0, the default, is the tuned order; 1 reverses it.  Every workgroup

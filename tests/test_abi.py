@@ -337,3 +337,36 @@ def test_launch_order_values(lib):
     assert lib.dit_attn_set_launch_order(1) == B.DIT_OK
     assert lib.dit_attn_set_launch_order(0) == B.DIT_OK
     assert B.dit_attn_last_error() == ""
+
+
+def _noalloc(lib, **kw):
+    a = dict(q=Q, k=K, v=V, wq=WQ, wk=WK, T=1, H=128, W=342, heads=4, d=96, theta=1e4, eps=1e-6, o=O, stream=None)
+    a.update(kw)
+    return lib.dit_attn_dense_noalloc(a["q"], a["k"], a["v"], a["wq"], a["wk"], a["T"], a["H"], a["W"], a["heads"],
+                                      a["d"], a["theta"], a["eps"], a["o"], a["stream"])
+
+
+@pytest.mark.parametrize("kw", [dict(), dict(T=1, H=128, W=512, heads=2, d=128), dict(T=31, H=48, W=84, heads=56)])
+def test_noalloc_rejects_calls_past_the_static_scratch(lib, kw):
+    """Sizes past the 64 MiB static scratch are refused on the host, before any HIP call: one tile image more
+    than fits at each head dim (4 x 342 blocks at 96, 2 x 512 at 128) and the full 5 s video layer."""
+    assert _noalloc(lib, **kw) == B.DIT_ERR_UNSUPPORTED
+    assert "static scratch" in B.dit_attn_last_error()
+    assert str(B.NOALLOC_SCRATCH_BYTES) in B.dit_attn_last_error()
+
+
+@pytest.mark.parametrize("kw,status,text", [
+    (dict(q=None), B.DIT_ERR_INVALID_ARG, "null"),
+    (dict(o=None), B.DIT_ERR_INVALID_ARG, "null"),
+    (dict(d=64), B.DIT_ERR_UNSUPPORTED, "head_dim"),
+    (dict(eps=float("nan")), B.DIT_ERR_INVALID_ARG, "eps"),
+])
+def test_noalloc_validation_errors(lib, kw, status, text):
+    assert _noalloc(lib, **kw) == status
+    assert text in B.dit_attn_last_error()
+
+
+def test_noalloc_scratch_size_matches_header():
+    text = open(HEADERS[0]).read()
+    assert re.search(r"#define DIT_ATTN_NOALLOC_SCRATCH_BYTES \(\(size_t\)64 << 20\)", text)
+    assert B.NOALLOC_SCRATCH_BYTES == 64 << 20
