@@ -5,7 +5,8 @@ A step is one full layer: dense attention over the whole token grid for all head
 seeded synthetic bf16 tensors already resident in HBM when the timed region
 starts.  Prints ONE JSON line.
 
-    python bench.py [--steps K] [--warmup W] [--workload v5|image|v5s|v10s|v10d|v5h7|v5w|v5sw|j_edit2|b_v5]
+    python bench.py [--steps K] [--warmup W]
+                    [--workload v5|image|v5s|v10s|v10d|v5h7|v5w|v5sw|v5o|v5so|v5d128|v5s128|j_edit2|b_v5]
                     [--no-cpu-baseline] [--calib-copy]
 """
 from __future__ import annotations
@@ -40,11 +41,18 @@ DESCR = {
     "v5d128": ("dense attention at head dim 128, 124,992 tokens, 42 heads x 128 (the same 5376 hidden width; "
                "RoPE chunks 44/42/42)"),
     "v5s128": ("route + block-sparse attention (sparsity 0.75) at head dim 128, 124,992 tokens, 42 heads x 128"),
-    "v5w": ("dense attention, 124,992 tokens, 56 heads x 96, norm weights 1.75(1+0.1N(0,1)): logits past the "
-            "static-shift bound, so the running-maximum softmax runs"),
+    "v5w": ("dense attention, 124,992 tokens, 56 heads x 96, norm weights 1.75(1+0.1N(0,1)): logit bound 59.6, "
+            "past what exp2 takes unshifted, so the static softmax subtracts a constant shift"),
     "v5sw": ("route + block-sparse attention (sparsity 0.75), 124,992 tokens, 56 heads x 96, norm weights "
-             "1.75(1+0.1N(0,1)) (running-maximum softmax)"),
+             "1.75(1+0.1N(0,1)) (static softmax with a constant shift)"),
+    "v5o": ("dense attention, 124,992 tokens, 56 heads x 96, w_q channel 0 at 6: logit bound 89.9, past the "
+            "static limit of 80, so the running-maximum softmax runs"),
+    "v5so": ("route + block-sparse attention (sparsity 0.75), 124,992 tokens, 56 heads x 96, w_q channel 0 at 6 "
+             "(running-maximum softmax)"),
     "s4": "dense attention, small grid 5x24x40 = 4,800 tokens, 2 heads x 96 (contract checks)",
+    "s4s": "route + block-sparse attention (sparsity 0.75), small grid 5x24x40, 2 heads x 96 (contract checks)",
+    "j_small": ("joint attention, 768 target queries against 1,314 keys (50 text + 2 reference images + target), "
+                "3 heads x 96 (contract checks)"),
     "b_mid": "operators around attention on 1,000 tokens, hidden 5376, FFN 14336 (contract checks)",
     "b_v5": ("operators around attention at 124,992 tokens, hidden 5376, FFN 14336: AdaLN update, gated "
              "residual + AdaLN update, SwiGLU, gated residual"),
@@ -65,25 +73,110 @@ def kernel_source_sha256(path: str = KERNEL_SRC) -> str:
     return hashlib.sha256(" ".join(code.split()).encode()).hexdigest()
 
 
-def softmax_mode(wq: np.ndarray, wk: np.ndarray, d: int) -> str:
-    """Which attention kernel does the work for these norm weights: "static" (exp2 of the logits with no
-    shift) when log2(e) sqrt(d) max_i u_i v_i, times a 2% margin, is at most 48 -- u_i, v_i being the larger
-    |weight| of channel pair i in w_q, w_k -- else "online" (running maximum).  Used to name the kernel."""
+def logit_bound(wq: np.ndarray, wk: np.ndarray, d: int) -> float:
+    """log2(e) sqrt(d) max_i u_i v_i times a 2% margin, u_i, v_i being the larger |weight| of channel pair i
+    in w_q, w_k: the bound on |logit| in base 2 that QK-RMSNorm and RoPE guarantee."""
     u = np.maximum(np.abs(wq[0::2]), np.abs(wq[1::2])).astype(np.float64)
     v = np.maximum(np.abs(wk[0::2]), np.abs(wk[1::2])).astype(np.float64)
-    bound = math.log2(math.e) * math.sqrt(d) * float(np.max(u * v)) * 1.02
-    return "static" if bound <= 48.0 else "online"
+    return math.log2(math.e) * math.sqrt(d) * float(np.max(u * v)) * 1.02
+
+
+def softmax_mode(wq: np.ndarray, wk: np.ndarray, d: int) -> str:
+    """Which attention kernel does the work for these norm weights: "static" (exp2 of the logits, less the
+    constant max(0, bound - 48)) when the logit bound is at most 80, else "online" (running maximum).  Used to
+    name the kernel."""
+    return "static" if logit_bound(wq, wk, d) <= 80.0 else "online"
 
 
 def log(msg):
     print(msg, file=sys.stderr, flush=True)
 
 
+class ClockSampler:
+    """Samples the GPU's graphics clock while the timed steps run, in a background thread: the mean of the eight
+    XCDs' current clocks from amdsmi's GPU metrics, else the current level of pp_dpm_sclk in sysfs.  Reports the
+    mean, min and max over the samples (MHz), or None where neither source is readable."""
+
+    def __init__(self, period_s: float = 0.02):
+        import threading
+        self.period = period_s
+        self.samples = []
+        self.source = None
+        self._stop = threading.Event()
+        self._thread = threading.Thread(target=self._run, daemon=True)
+        self._read = self._open()
+
+    def _open(self):
+        try:
+            import amdsmi
+            amdsmi.amdsmi_init()
+            h = amdsmi.amdsmi_get_processor_handles()[0]
+
+            def read():
+                c = [int(v) for v in amdsmi.amdsmi_get_gpu_metrics_info(h)["current_gfxclks"]
+                     if isinstance(v, (int, float)) and 0 < v < 10000]
+                return sum(c) / len(c) if c else None
+            if read() is not None:
+                self.source = "amdsmi gpu metrics: mean of the XCDs' current_gfxclks"
+                return read
+        except Exception:
+            pass
+        import glob
+        for path in sorted(glob.glob("/sys/class/drm/card*/device/pp_dpm_sclk")):
+            def read(path=path):
+                for line in open(path).read().splitlines():
+                    if line.rstrip().endswith("*"):
+                        return float(re.findall(r"(\d+)\s*[Mm]hz", line)[0])
+                return None
+            try:
+                if read() is not None:
+                    self.source = f"sysfs {path} (current level)"
+                    return read
+            except Exception:
+                continue
+        return None
+
+    def _run(self):
+        while not self._stop.is_set():
+            try:
+                v = self._read()
+                if v is not None:
+                    self.samples.append(v)
+            except Exception:
+                return
+            self._stop.wait(self.period)
+
+    def __enter__(self):
+        if self._read is not None:
+            self._thread.start()
+        return self
+
+    def __exit__(self, *exc):
+        self._stop.set()
+        if self._thread.is_alive():
+            self._thread.join()
+
+    def summary(self):
+        if not self.samples:
+            return None
+        a = np.array(self.samples)
+        return {"mean_mhz": round(float(a.mean()), 1), "median_mhz": round(float(np.median(a)), 1),
+                "min_mhz": round(float(a.min()), 1), "max_mhz": round(float(a.max()), 1), "samples": int(a.size),
+                "source": self.source}
+
+
+def timing_summary(ms):
+    """Mean, median and min of per-step event timings (ms)."""
+    a = np.asarray(ms, dtype=np.float64)
+    return {"mean": round(float(a.mean()), 4), "median": round(float(np.median(a)), 4), "min": round(float(a.min()), 4)}
+
+
 def sample_blocks(nb: int, count: int = 8, seed: int = 1234):
     """Query blocks the oracle checks: first, last (ragged), middle and seeded random ones."""
     rng = np.random.default_rng(seed)
-    fixed = [0, nb - 1, nb // 2]
-    rest = [int(b) for b in rng.choice(np.setdiff1d(np.arange(nb), fixed), size=max(0, count - 3), replace=False)]
+    fixed = sorted(set([0, nb - 1, nb // 2]))
+    others = np.setdiff1d(np.arange(nb), fixed)
+    rest = [int(b) for b in rng.choice(others, size=min(len(others), max(0, count - len(fixed))), replace=False)]
     return sorted(set(fixed + rest))[:count]
 
 
@@ -122,14 +215,16 @@ def bench_joint(args, torch, dit):
         call()
     torch.cuda.synchronize()
     events = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(args.steps)]
-    t0 = time.perf_counter()
-    for i in range(args.steps):
-        events[i][0].record(stream)
-        call()
-        events[i][1].record(stream)
-    torch.cuda.synchronize()
-    ms_step = (time.perf_counter() - t0) * 1e3 / args.steps
-    ms_call = float(np.mean([e[0].elapsed_time(e[1]) for e in events]))
+    with ClockSampler() as clk:
+        t0 = time.perf_counter()
+        for i in range(args.steps):
+            events[i][0].record(stream)
+            call()
+            events[i][1].record(stream)
+        torch.cuda.synchronize()
+        ms_step = (time.perf_counter() - t0) * 1e3 / args.steps
+    call_ms = [e[0].elapsed_time(e[1]) for e in events]
+    ms_call = float(np.mean(call_ms))
     flops = 4.0 * wl.Nq * wl.Nkv * wl.head_dim * wl.heads
     tflops = flops / (ms_step * 1e-3) / 1e12
     result = {
@@ -143,8 +238,41 @@ def bench_joint(args, torch, dit):
                      "unit": "TFLOP/s", "frac": round(flops / (ms_call * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4),
                      "traffic": None, "kernel": f"attn_static_kernel<{wl.head_dim}, false>", "kernel_ms": round(ms_call, 3),
                      "timed": "whole call: K^/V fragment prepass + attention kernels", "flops_per_launch": flops},
+        "call_ms": timing_summary(call_ms),
+        "sclk": clk.summary(),
     }
+    # parity on sampled query rows of four heads, and the CPU baseline: the fp64 oracle on the same rows
+    heads = sorted(set([0, wl.heads // 3, (2 * wl.heads) // 3, wl.heads - 1]))
+    nqb = -(-wl.Nq // 128)
+    blocks = sample_blocks(nqb)
+    rows = np.concatenate([np.arange(b * 128, min(wl.Nq, (b + 1) * 128)) for b in blocks])
+    o_np = o[torch.from_numpy(rows).to(dev)][:, heads].float().cpu().numpy()
+    if not args.no_cpu_baseline:
+        from oracle import attention as A
+        cores = len(os.sched_getaffinity(0))
+        t0 = time.perf_counter()
+        ref = A.attention_joint(x.q, x.k, x.v, x.wq, x.wk, x.q_pos, x.k_pos, wl.theta, wl.eps, heads=heads, rows=rows)
+        t_cpu = time.perf_counter() - t0
+        err = np.abs(o_np.astype(np.float64) - ref)
+        frac = (len(rows) * len(heads)) / (wl.Nq * wl.heads)
+        result["parity"] = {"rows": int(len(rows)), "heads": heads, "blocks": blocks, "max_abs": float(err.max()),
+                            "rel_l2": float(np.linalg.norm(err) / np.linalg.norm(ref))}
+        result["cpu_baseline"] = {
+            "value": round(flops * frac / t_cpu / 1e12, 5), "unit": "TFLOP/s", "cores": blas_threads() or cores,
+            "kind": "oracle",
+            "sample": (f"fp64 numpy oracle on {len(blocks)} query blocks x {len(heads)} heads ({len(rows)} rows each, "
+                       f"all {wl.Nkv} keys): {t_cpu:.1f} s for {frac:.5f} of the layer; full layer extrapolated to "
+                       f"{t_cpu / frac:.0f} s"),
+            "host_cores": cores}
     print(json.dumps(result), flush=True)
+
+
+def blas_threads():
+    try:
+        from threadpoolctl import threadpool_info
+        return max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
+    except Exception:
+        return None
 
 
 def bench_block(args, torch, dit):
@@ -177,14 +305,15 @@ def bench_block(args, torch, dit):
             f()
     torch.cuda.synchronize()
     ev = [[torch.cuda.Event(enable_timing=True) for _ in range(len(ops) + 1)] for _ in range(args.steps)]
-    t0 = time.perf_counter()
-    for i in range(args.steps):
-        ev[i][0].record(stream)
-        for j, (_, f, _) in enumerate(ops):
-            f()
-            ev[i][j + 1].record(stream)
-    torch.cuda.synchronize()
-    ms_step = (time.perf_counter() - t0) * 1e3 / args.steps
+    with ClockSampler() as clk:
+        t0 = time.perf_counter()
+        for i in range(args.steps):
+            ev[i][0].record(stream)
+            for j, (_, f, _) in enumerate(ops):
+                f()
+                ev[i][j + 1].record(stream)
+        torch.cuda.synchronize()
+        ms_step = (time.perf_counter() - t0) * 1e3 / args.steps
     per = {name: float(np.mean([e[j].elapsed_time(e[j + 1]) for e in ev])) for j, (name, _, _) in enumerate(ops)}
     if args.calib_copy:
         a = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
@@ -219,6 +348,8 @@ def bench_block(args, torch, dit):
                      "frac": round(dom_gbs / PEAK_HBM_GBS, 4), "traffic": traffic,
                      "kernel": f"swiglu_kernel<{min(8, -(-wl.ffn // 8 // 256))}>",
                      "kernel_ms": round(per[dom], 4), "bytes_per_launch": dom_bytes},
+        "call_ms": {n: timing_summary([e[j].elapsed_time(e[j + 1]) for e in ev]) for j, (n, _, _) in enumerate(ops)},
+        "sclk": clk.summary(),
     }
     if not args.no_cpu_baseline:
         from oracle import block_ops as O
@@ -309,18 +440,21 @@ def main():
     nev = 3 if sparse else 2
     events = [[torch.cuda.Event(enable_timing=True) for _ in range(nev)] for _ in range(args.steps)]
     torch.cuda.synchronize()
-    t_start = time.perf_counter()
-    for i in range(args.steps):
-        step(events[i])
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - t_start
+    with ClockSampler() as clk:
+        t_start = time.perf_counter()
+        for i in range(args.steps):
+            step(events[i])
+        torch.cuda.synchronize()
+        wall = time.perf_counter() - t_start
     ms_step = wall * 1e3 / args.steps
     if sparse:
-        ms_route = float(np.mean([e[0].elapsed_time(e[1]) for e in events]))
-        ms_attn = float(np.mean([e[1].elapsed_time(e[2]) for e in events]))
+        route_ms = [e[0].elapsed_time(e[1]) for e in events]
+        attn_ms = [e[1].elapsed_time(e[2]) for e in events]
     else:
-        ms_attn = float(np.mean([e[0].elapsed_time(e[1]) for e in events]))
-        ms_route = 0.0
+        route_ms = []
+        attn_ms = [e[0].elapsed_time(e[1]) for e in events]
+    ms_attn = float(np.mean(attn_ms))
+    ms_route = float(np.mean(route_ms)) if route_ms else 0.0
     log(f"timed {args.steps} steps: {ms_step:.2f} ms/step (events: attn {ms_attn:.2f} ms, route {ms_route:.2f} ms)")
 
     if args.calib_copy:
@@ -361,7 +495,8 @@ def main():
         "vs_baseline": None,
         "dtype": "bf16",
         "data": ("synthetic (seeded N(0,1) bf16 Q/K/V, video grids plus smooth sinusoid component; norm weights "
-                 + ("1+0.1N(0,1))" if wl.weight_scale == 1.0 else f"{wl.weight_scale:g}(1+0.1N(0,1)))")),
+                 + ("1+0.1N(0,1)" if wl.weight_scale == 1.0 else f"{wl.weight_scale:g}(1+0.1N(0,1))")
+                 + (f", w_q channel 0 at {wl.wq_spike:g})" if wl.wq_spike else ")")),
         "config": {"workload": f"{wl.name}: {DESCR[wl.name]}", "tokens": N, "heads": H, "head_dim": d,
                    "grid": [wl.T, wl.H, wl.W], "mode": wl.mode, "sparsity": wl.sparsity if sparse else None},
         "ms_per_layer": round(ms_step, 3),
@@ -371,10 +506,14 @@ def main():
                      "kernel": f"attn_{softmax_mode(x.wq, x.wk, d)}_kernel<{d}, " + ("true>" if sparse else "false>"),
                      "timed": "whole call: K^/V fragment prepass + attention kernels",
                      "kernel_ms": round(ms_attn, 3), "flops_per_launch": flops},
+        # per-step event timings of the attention call (and of the router call for sparse workloads)
+        "call_ms": timing_summary(attn_ms),
+        "sclk": clk.summary(),
     }
     if sparse:
         result["dense_equivalent_tflops"] = round(dense_flops / (ms_step * 1e-3) / 1e12, 2)
         result["route_ms"] = round(ms_route, 3)
+        result["route_call_ms"] = timing_summary(route_ms)
         result["kept_fraction"] = round(float(mask_np.mean()), 4)
 
     # ---- parity on sampled query blocks and the CPU baseline (fp64 oracle on host cores)
@@ -384,13 +523,20 @@ def main():
     o_np = o[torch.from_numpy(rows).to(dev)][:, heads].float().cpu().numpy()
     if not args.no_cpu_baseline:
         from oracle import attention as A
-        try:
-            from threadpoolctl import threadpool_info
-            blas_threads = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
-        except Exception:
-            blas_threads = None
         cores = len(os.sched_getaffinity(0))
         oracle_mask = mask_np
+        mask_check = None
+        if sparse:
+            # the router's mask of head 0 against the oracle's (fp32 specification, every row), and O of head 0
+            # evaluated on the oracle's mask; the other sampled heads on the router's
+            from oracle import router as R
+            t0 = time.perf_counter()
+            m0 = R.route_mask(x.q, x.k, x.wq, x.wk, wl.T, wl.H, wl.W, wl.sparsity, wl.theta, wl.eps, heads=[0])[0]
+            t_route = time.perf_counter() - t0
+            bad = int(np.any(m0 != mask_np[0], axis=1).sum())
+            oracle_mask = mask_np.copy()
+            oracle_mask[0] = m0
+            mask_check = {"head": 0, "rows": int(wl.nb), "rows_mismatched": bad, "oracle_s": round(t_route, 2)}
         t0 = time.perf_counter()
         ref = A.attention(x.q, x.k, x.v, x.wq, x.wk, wl.T, wl.H, wl.W, wl.theta, wl.eps, heads=heads, rows=rows,
                           mask=oracle_mask)
@@ -407,9 +553,11 @@ def main():
         err = np.abs(o_np.astype(np.float64) - ref)
         result["parity"] = {"rows": int(len(rows)), "heads": heads, "blocks": blocks,
                             "max_abs": float(err.max()), "rel_l2": float(np.linalg.norm(err) / np.linalg.norm(ref)),
-                            "mask_source": "gpu router" if sparse else None}
+                            "mask_source": ("oracle router for head 0, gpu router for the others" if sparse
+                                            else None),
+                            "router_mask_vs_oracle": mask_check}
         result["cpu_baseline"] = {
-            "value": round(cpu_tflops, 5), "unit": "TFLOP/s", "cores": blas_threads or cores, "kind": "oracle",
+            "value": round(cpu_tflops, 5), "unit": "TFLOP/s", "cores": blas_threads() or cores, "kind": "oracle",
             "sample": (f"fp64 numpy oracle on {len(blocks)} query blocks x {len(heads)} heads "
                        f"({len(rows)} rows each, all keys): {t_cpu:.1f} s for {frac_rows:.5f} of the layer; "
                        f"full layer extrapolated to {t_cpu / frac_rows:.0f} s"),

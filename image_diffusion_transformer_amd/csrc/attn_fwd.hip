@@ -33,8 +33,9 @@
 //    already the B operand of the next MFMA after bf16 packing.
 //  * O^T += V^T P^T with the same MFMA, V^T fragments read from LDS with one
 //    16-byte load per lane.
-//  * Static-shift softmax when the QK-RMSNorm logit bound allows it (p = exp2(S),
-//    no running max); otherwise an online softmax in base 2 whose running max
+//  * Static-shift softmax when the QK-RMSNorm logit bound B allows it (B <= 80 in
+//    base 2: p = exp2(S - c), c = max(0, B - 48) taken as the first S MFMA's
+//    accumulator input, no running max); otherwise an online softmax in base 2 whose running max
 //    only moves (and O, l are rescaled) when a lane's block sum of p passes 2^8,
 //    so every p stays <= 2^8 and the block max is computed only then; the final
 //    O / l is exact for any stale max.
@@ -195,16 +196,21 @@ __device__ __forceinline__ u32x4 norm_rope_chunk(u32x4 raw, float r, float scale
 // Softmax modes.  QK-RMSNorm bounds every logit.  RoPE rotates each channel pair (2i, 2i+1) rigidly, so
 // pair i of q^ . k^ is at most |a_i| |b_i|, with a_i the normalised q pair times its weights:
 // |a_i| <= u_i |x_i|, u_i = max(|w_q,2i|, |w_q,2i+1|) (v_i likewise for k).  Summing and Cauchy-Schwarz
-// over the pairs (|x| <= sqrt(d) after the norm): |q^ . k^| / sqrt(d) <= sqrt(d) max_i u_i v_i, never
-// looser than sqrt(d) max|w_q| max|w_k|.  When that bound, in base-2 units, is at most kStaticBound,
-// exp2(S) with no shift can neither overflow nor underflow for any input, and the shift cancels in
-// O / rowsum: no running max, no subtraction, no rescale.  Otherwise the online (running-max) softmax
-// runs.
+// over the pairs (|x| <= sqrt(d) after the norm): |q^ . k^| / sqrt(d) <= sqrt(d) max_i u_i v_i = B (in
+// base-2 units), never looser than sqrt(d) max|w_q| max|w_k|.  When B <= kStaticBound, the static mode
+// takes p = exp2(S - c) with the constant shift c = max(0, B - 48): every exponent lies in
+// [48 - 2B, 48], so p is a normal bf16 / fp32 number, never overflowing (p <= 2^48) nor flushed
+// (p >= 2^-112), for any input, and the shift cancels in O / rowsum.  The shift costs nothing: it is
+// the accumulator input of each key sub-block's first S MFMA.  No running max, no subtraction, no
+// rescale; the fp32 sums stay finite while N max|V| < 2^80.  Otherwise (B > kStaticBound, or NaN
+// weights) the online (running-max) softmax runs.
 enum SoftmaxMode { kStatic = 0, kOnline = 1 };
-constexpr float kStaticBound = 48.0f;
+constexpr float kStaticBound = 80.0f;
+constexpr float kUnshiftedBound = 48.0f;
 
+// Shift of the static mode for these weights (0 while B <= 48).
 template <int D>
-__device__ __forceinline__ bool static_bound_holds(const AttnArgs& a, int lane) {
+__device__ __forceinline__ float logit_bound(const AttnArgs& a, int lane, bool& bad_out) {
   float m = 0.f;
   int bad = 0;                                     // a NaN weight sends the call to the online kernel
   for (int i = lane; i < D / 2; i += 64) {
@@ -221,7 +227,15 @@ __device__ __forceinline__ bool static_bound_holds(const AttnArgs& a, int lane) 
   }
   // 1.02 covers the approximate reciprocal square root, the rotation and the bf16 rounding of q^, k^.
   const float sqrt_d = D == 96 ? 9.797958971132712f : 11.313708498984761f;
-  const float bound = 1.4426950408889634f * sqrt_d * m * 1.02f;
+  bad_out = bad != 0;
+  return 1.4426950408889634f * sqrt_d * m * 1.02f;
+}
+
+template <int D>
+__device__ __forceinline__ bool static_bound_holds(const AttnArgs& a, int lane, float& shift) {
+  bool bad;
+  const float bound = logit_bound<D>(a, lane, bad);
+  shift = fmaxf(bound - kUnshiftedBound, 0.0f);
   return !bad && bound <= kStaticBound;            // false for infinite weights too
 }
 
@@ -406,7 +420,8 @@ __device__ __forceinline__ void softmax_online(f32x16 (&S)[QB], bool ragged, int
   }
 }
 
-// Static-shift softmax of one sub-block: p = exp2(S).  The caller has masked keys past the grid to -inf.
+// Static-shift softmax of one sub-block: p = exp2(S), S already holding the logits less the constant shift.
+// The caller has masked keys past the grid to -inf.
 template <int QB, int QM = (1 << QB) - 1>
 __device__ __forceinline__ void softmax_static(const f32x16 (&S)[QB], float (&l)[QB], bf16x8 (&P)[QB][2]) {
 #pragma unroll
@@ -589,13 +604,14 @@ __device__ __forceinline__ void tile_barrier() {
 // of the next tile's fragment image into the other LDS stage, then per 32-key sub-block: S MFMAs, softmax,
 // PV MFMAs.  One barrier per tile.  Block-sparse tiles are computed only for the query blocks whose
 // router block keeps them (activity mask QM of the wave's blocks).
-// S^T of sub-block kb with its first two K^ fragments already in registers (kp).
+// S^T - c of sub-block kb with its first two K^ fragments already in registers (kp); negc holds -c in
+// every element and is the accumulator input of the first MFMA.
 template <int D, int QB, int QM>
 __device__ __forceinline__ void qk_block_pre(const uint16_t* T_, int kb, int lane, const bf16x8 (&qf)[QB][Head<D>::KS],
-                                             const bf16x8 (&kp)[2], f32x16 (&S)[QB]) {
+                                             const bf16x8 (&kp)[2], const f32x16& negc, f32x16 (&S)[QB]) {
   constexpr int KS = Head<D>::KS;
 #pragma unroll
-  for (int qb = 0; qb < QB; ++qb) S[qb] = f32x16{};
+  for (int qb = 0; qb < QB; ++qb) S[qb] = negc;
 #pragma unroll
   for (int ks = 0; ks < KS; ++ks) {
     const bf16x8 ka = ks < 2 ? kp[ks] : *(const bf16x8*)(T_ + (kb * KS + ks) * kFrag + lane * 8);
@@ -609,7 +625,7 @@ __device__ __forceinline__ void qk_block_pre(const uint16_t* T_, int kb, int lan
 template <int D, int QB, int QM, int MODE>
 __device__ __forceinline__ void tile_body(const uint16_t* T_, int lane, const bf16x8 (&qf)[QB][Head<D>::KS],
                                           f32x16 (&acc)[QB][Head<D>::DB], float (&m)[QB], float (&l)[QB],
-                                          bool ragged, int key0, int N) {
+                                          const f32x16& negc, bool ragged, int key0, int N) {
   constexpr int KS = Head<D>::KS;
   if constexpr (MODE == kStatic) {
     // The first two K^ fragments of each sub-block are read while the previous sub-block's S MFMAs
@@ -621,7 +637,7 @@ __device__ __forceinline__ void tile_body(const uint16_t* T_, int lane, const bf
 #pragma unroll 1
     for (int kb = 0; kb < BK / 32; ++kb) {
       f32x16 S[QB];
-      qk_block_pre<D, QB, QM>(T_, kb, lane, qf, kp, S);
+      qk_block_pre<D, QB, QM>(T_, kb, lane, qf, kp, negc, S);
       const int nk = kb + 1 < BK / 32 ? kb + 1 : kb;   // the last sub-block re-reads its own (unused)
       kp[0] = *(const bf16x8*)(T_ + (nk * KS + 0) * kFrag + lane * 8);
       kp[1] = *(const bf16x8*)(T_ + (nk * KS + 1) * kFrag + lane * 8);
@@ -655,7 +671,11 @@ __device__ __forceinline__ void attn_kernel_body(const AttnArgs& a, uint16_t* sK
   TileIter ti;
   if (!tile_iter<SPARSE>(a, ti)) return;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  if (static_bound_holds<D>(a, lane) != (MODE == kStatic)) return;   // the other kernel handles these weights
+  float shift;
+  if (static_bound_holds<D>(a, lane, shift) != (MODE == kStatic)) return;   // the other kernel takes these weights
+  f32x16 negc;
+#pragma unroll
+  for (int i = 0; i < 16; ++i) negc[i] = -shift;
   const int N = a.nk, nt = ti.ntiles;
   int rbit[QB];
 #pragma unroll
@@ -709,15 +729,15 @@ __device__ __forceinline__ void attn_kernel_body(const AttnArgs& a, uint16_t* sK
     const bool ragged = (tile + 1) * BK > N;
     if constexpr (SPARSE && QB == 2) {
       if (qm == 3)
-        tile_body<D, QB, 3, MODE>(T_, lane, qf, acc, m, l, ragged, tile * BK, N);
+        tile_body<D, QB, 3, MODE>(T_, lane, qf, acc, m, l, negc, ragged, tile * BK, N);
       else if (qm == 1)
-        tile_body<D, QB, 1, MODE>(T_, lane, qf, acc, m, l, ragged, tile * BK, N);
+        tile_body<D, QB, 1, MODE>(T_, lane, qf, acc, m, l, negc, ragged, tile * BK, N);
       else if (qm == 2)
-        tile_body<D, QB, 2, MODE>(T_, lane, qf, acc, m, l, ragged, tile * BK, N);
+        tile_body<D, QB, 2, MODE>(T_, lane, qf, acc, m, l, negc, ragged, tile * BK, N);
     } else if constexpr (SPARSE) {
-      if (qm != 0) tile_body<D, QB, (1 << QB) - 1, MODE>(T_, lane, qf, acc, m, l, ragged, tile * BK, N);
+      if (qm != 0) tile_body<D, QB, (1 << QB) - 1, MODE>(T_, lane, qf, acc, m, l, negc, ragged, tile * BK, N);
     } else {
-      tile_body<D, QB, (1 << QB) - 1, MODE>(T_, lane, qf, acc, m, l, ragged, tile * BK, N);
+      tile_body<D, QB, (1 << QB) - 1, MODE>(T_, lane, qf, acc, m, l, negc, ragged, tile * BK, N);
     }
     tile_barrier();
     e_cur = e_nxt;

@@ -50,6 +50,7 @@ class Workload:
     fp32_inputs: bool = False    # the tiny grid also keeps its float32 draw
     head_dim: int = HEAD_DIM     # 96 (the model's); 128 for the head-dim-128 instantiation
     weight_scale: float = 1.0    # RMSNorm weights are weight_scale * (1 + 0.1 N(0, 1))
+    wq_spike: float = 0.0        # if nonzero, w_q channel 0 is set to this value (one large channel)
     notes: str = field(default="", compare=False)
 
     @property
@@ -83,6 +84,8 @@ WORKLOADS = {
         Workload("s2", 3, 16, 16, 3, seed=11, smooth=True, notes="N=768 (6 full blocks)"),
         Workload("s3", 4, 12, 20, 4, seed=12, smooth=True, notes="N=960 (tail 64)"),
         Workload("s4", 5, 24, 40, 2, seed=13, smooth=True, notes="N=4800 (tail 64), 38 blocks"),
+        Workload("s4s", 5, 24, 40, 2, seed=13, smooth=True, mode="sparse", sparsity=0.75,
+                 notes="s4's tensors, block-sparse at sparsity 0.75"),
         # head dim 128 (42 heads x 128 = the same 5376 hidden width)
         Workload("t128", 2, 4, 4, 2, seed=30, smooth=False, head_dim=128, notes="2x4x4 grid, head dim 128"),
         Workload("s1_128", 2, 10, 10, 2, seed=31, smooth=True, head_dim=128, notes="N=200 (tail 72), head dim 128"),
@@ -93,11 +96,17 @@ WORKLOADS = {
         Workload("v5s128", 31, 48, 84, 42, seed=34, smooth=True, head_dim=128, mode="sparse", sparsity=0.75,
                  notes="same tensors as v5d128, block-sparse at sparsity 0.75"),
         # norm weights 1.75 times as large: the logit bound (59.6 in base 2) is past what exp2 takes without
-        # a shift, so the kernels keep a running maximum (the general softmax path)
+        # a shift, so the static mode subtracts a constant (bound - 48) from every logit
         Workload("v5w", 31, 48, 84, 56, seed=2, smooth=True, weight_scale=1.75,
                  notes="same tensors as v5, norm weights 1.75(1 + 0.1 N(0,1)), dense"),
         Workload("v5sw", 31, 48, 84, 56, seed=2, smooth=True, weight_scale=1.75, mode="sparse", sparsity=0.75,
                  notes="same tensors as v5, norm weights 1.75(1 + 0.1 N(0,1)), block-sparse at sparsity 0.75"),
+        # w_q channel 0 at 6: the pairwise logit bound (about 90 in base 2) is past the static mode's limit of 80,
+        # so the running-maximum kernels run, while the logits themselves stay moderate
+        Workload("v5o", 31, 48, 84, 56, seed=2, smooth=True, wq_spike=6.0,
+                 notes="same tensors as v5, w_q channel 0 at 6, dense"),
+        Workload("v5so", 31, 48, 84, 56, seed=2, smooth=True, wq_spike=6.0, mode="sparse", sparsity=0.75,
+                 notes="same tensors as v5, w_q channel 0 at 6, block-sparse at sparsity 0.75"),
     ]
 }
 
@@ -171,7 +180,11 @@ def norm_weights(wl: Workload | str) -> tuple[np.ndarray, np.ndarray]:
     """The workload's RMSNorm weights (w_q, w_k), float32 [head_dim] each, without drawing Q/K/V."""
     if isinstance(wl, str):
         wl = WORKLOADS[wl]
-    return _weights(wl.seed, wl.head_dim, wl.weight_scale)
+    wq, wk = _weights(wl.seed, wl.head_dim, wl.weight_scale)
+    if wl.wq_spike:
+        wq = wq.copy()
+        wq[0] = np.float32(wl.wq_spike)
+    return wq, wk
 
 
 def _fill_chunk(wl: Workload, tensor: int, chunk: int, smooth, out_bits, out_f32):

@@ -11,7 +11,7 @@ pytestmark = pytest.mark.gpu
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 
 
-@pytest.mark.parametrize("workload", ["s4", "b_mid"])
+@pytest.mark.parametrize("workload", ["s4", "s4s", "j_small", "b_mid"])
 def test_bench_prints_one_contract_line(workload):
     r = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--workload", workload, "--steps", "2",
                         "--warmup", "1"], capture_output=True, text=True, timeout=300, cwd=ROOT)
@@ -30,6 +30,21 @@ def test_bench_prints_one_contract_line(workload):
     assert roof["bound"] in ("mfma", "hbm") and 0 < roof["frac"] < 1
     cpu = res["cpu_baseline"]
     assert cpu["kind"] == "oracle" and cpu["cores"] >= 1 and cpu["value"] > 0 and cpu["sample"]
+    # per-step timings: mean, median and min of the event-timed calls
+    timings = res["call_ms"] if not workload.startswith("b_") else next(iter(res["call_ms"].values()))
+    assert 0 < timings["min"] <= timings["median"] and timings["min"] <= timings["mean"]
+    # the graphics clock sampled during the timed steps (amdsmi or sysfs on the GPU machine)
+    assert "sclk" in res
+    if res["sclk"] is not None:
+        assert 0 < res["sclk"]["min_mhz"] <= res["sclk"]["mean_mhz"] <= res["sclk"]["max_mhz"] < 5000
+        assert res["sclk"]["samples"] >= 1 and res["sclk"]["source"]
+    if not workload.startswith("b_"):
+        par = res["parity"]
+        assert par["max_abs"] <= 2e-2 and par["rel_l2"] <= 1e-2, par
+    if workload == "s4s":
+        chk = res["parity"]["router_mask_vs_oracle"]
+        assert chk["head"] == 0 and chk["rows"] == 38 and chk["rows_mismatched"] == 0
+        assert res["route_call_ms"]["min"] > 0
 
 
 def test_bench_refuses_several_gpus():

@@ -10,6 +10,8 @@ from oracle import attention as A
 from oracle import router as R
 from synth import WORKLOADS, bf16_bits_to_f32, f32_to_bf16_bits, make_inputs, make_joint_inputs
 
+from bounds import STATIC_LIMIT, pair_bound, spike_to_bound
+
 pytestmark = pytest.mark.gpu
 DEV = torch.device("cuda:0")
 MAX_ABS, REL_L2 = 2e-2, 1e-2
@@ -47,13 +49,11 @@ def test_dense_d128_all_rows(name):
 def test_dense_d128_online_mode():
     x = make_inputs("s3_128")
     wl = x.workload
-    q, k, v, wq, wk = upload(x)
-    wq2 = wq.clone()
-    wq2[7] = 4.0                      # logit bound > 48: the running-max kernel runs
-    o = dit.dit_attn_dense(q, k, v, wq2, wk, (wl.T, wl.H, wl.W), wl.theta, wl.eps)
+    q, k, v, _, wk = upload(x)
+    wqn = spike_to_bound(x.wq, x.wk, 128, 7)     # logit bound 90 > 80: the running-max kernel runs
+    assert pair_bound(wqn, x.wk, 128) > STATIC_LIMIT
+    o = dit.dit_attn_dense(q, k, v, torch.from_numpy(wqn).to(DEV), wk, (wl.T, wl.H, wl.W), wl.theta, wl.eps)
     torch.cuda.synchronize()
-    wqn = x.wq.copy()
-    wqn[7] = 4.0
     ref = A.attention(x.q, x.k, x.v, wqn, x.wk, wl.T, wl.H, wl.W, wl.theta, wl.eps)
     check_close(o.float().cpu().numpy(), ref, "dense d128 online")
 

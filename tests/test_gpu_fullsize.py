@@ -8,6 +8,7 @@ import torch
 import image_diffusion_transformer_amd as dit
 from oracle import attention as A
 from oracle import router as R
+from bounds import STATIC_LIMIT, UNSHIFTED_LIMIT, pair_bound
 from synth import WORKLOADS, make_inputs, norm_weights
 
 pytestmark = pytest.mark.gpu
@@ -112,25 +113,26 @@ def test_route_sparse_and_dense_full_size_v10():
     check(got, ref, f"dense v10d blocks {blocks}")
 
 
-def test_running_max_full_size_v5w(v5):
-    """The same 5 s video tensors with norm weights 1.75(1 + 0.1 N(0,1)), whose logit bound is past the
-    static shift: dense and route + block-sparse attention run the running-maximum kernels, at full size."""
+def _dense_and_sparse_full_size(v5, dense_name, sparse_name, seed):
+    """Dense, then route + block-sparse attention on the 5 s video tensors with the norm weights of the named
+    workloads, checked on sampled query blocks of two heads (the sparse O on the oracle's mask, which must
+    equal the router's bit for bit)."""
     x, (q, k, v, _, _) = v5
-    wl = WORKLOADS["v5w"]
+    wl = WORKLOADS[dense_name]
     wq_np, wk_np = norm_weights(wl)
     wq, wk = torch.from_numpy(wq_np).to(DEV), torch.from_numpy(wk_np).to(DEV)
     g = (wl.T, wl.H, wl.W)
-    print("case dense full v5w", flush=True)
+    print(f"case dense full {dense_name}", flush=True)
     o = dit.dit_attn_dense(q, k, v, wq, wk, g, wl.theta, wl.eps)
     torch.cuda.synchronize()
-    blocks, rows = sample_rows(wl.nb, wl.N, seed=77)
+    blocks, rows = sample_rows(wl.nb, wl.N, seed=seed)
     heads = [3, 41]
     got = o[torch.from_numpy(rows).to(DEV)][:, heads].float().cpu().numpy()
     ref = A.attention(x.q, x.k, x.v, wq_np, wk_np, wl.T, wl.H, wl.W, wl.theta, wl.eps, heads=heads, rows=rows)
-    check(got, ref, f"dense v5w blocks {blocks}")
+    check(got, ref, f"dense {dense_name} blocks {blocks}")
 
-    sw = WORKLOADS["v5sw"]
-    print("case route+sparse full v5sw", flush=True)
+    sw = WORKLOADS[sparse_name]
+    print(f"case route+sparse full {sparse_name}", flush=True)
     ws = dit.workspace_for(q, g)
     mask = dit.dit_attn_route(q, k, wq, wk, g, sw.sparsity, sw.theta, sw.eps, workspace=ws)
     o = dit.dit_attn_block_sparse(q, k, v, wq, wk, g, mask, sw.theta, sw.eps, o=o, workspace=ws)
@@ -144,4 +146,21 @@ def test_running_max_full_size_v5w(v5):
     full_mask[heads] = m_ref
     ref = A.attention(x.q, x.k, x.v, wq_np, wk_np, sw.T, sw.H, sw.W, sw.theta, sw.eps, heads=heads, rows=rows,
                       mask=full_mask)
-    check(got, ref, f"sparse v5sw blocks {blocks}")
+    check(got, ref, f"sparse {sparse_name} blocks {blocks}")
+
+
+def test_shifted_static_full_size_v5w(v5):
+    """The same 5 s video tensors with norm weights 1.75(1 + 0.1 N(0,1)), whose logit bound (59.6) is past what
+    exp2 takes unshifted: dense and route + block-sparse attention run the static kernels with their constant
+    shift of the logits, at full size."""
+    wq, wk = norm_weights("v5w")
+    assert UNSHIFTED_LIMIT < pair_bound(wq, wk, 96) <= STATIC_LIMIT
+    _dense_and_sparse_full_size(v5, "v5w", "v5sw", seed=77)
+
+
+def test_running_max_full_size_v5o(v5):
+    """The same tensors with w_q channel 0 at 6, a logit bound (89.9) past the static limit: dense and
+    route + block-sparse attention run the running-maximum kernels, at full size."""
+    wq, wk = norm_weights("v5o")
+    assert pair_bound(wq, wk, 96) > STATIC_LIMIT
+    _dense_and_sparse_full_size(v5, "v5o", "v5so", seed=78)

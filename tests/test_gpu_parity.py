@@ -12,6 +12,8 @@ from oracle import attention as A
 from oracle import router as R
 from synth import WORKLOADS, custom_workload, f32_to_bf16_bits, make_inputs
 
+from bounds import STATIC_LIMIT, UNSHIFTED_LIMIT, pair_bound, spike_to_bound
+
 pytestmark = pytest.mark.gpu
 DEV = torch.device("cuda:0")
 MAX_ABS, REL_L2 = 2e-2, 1e-2
@@ -109,35 +111,41 @@ def aligned_keys(x, wl, qrows, krows, head):
 
 
 def static_shift_bound(wq, wk, d=96):
-    """The kernels' test for the static-shift softmax, restated: the base-2 logit bound
+    """The kernels' test for the softmax mode, restated: the base-2 logit bound
     log2(e) sqrt(d) max_i u_i v_i (u_i, v_i the larger |weight| of channel pair i of w_q, w_k), with
-    the kernels' 2% margin; at most 48 selects the static kernel."""
-    u = np.maximum(np.abs(wq[0::2]), np.abs(wq[1::2])).astype(np.float64)
-    v = np.maximum(np.abs(wk[0::2]), np.abs(wk[1::2])).astype(np.float64)
-    return np.log2(np.e) * np.sqrt(d) * float(np.max(u * v)) * 1.02
+    the kernels' 2% margin; up to 48 the static kernel takes exp2 of the logits, up to 80 it subtracts the
+    constant bound - 48 first, past 80 the running-maximum kernel runs."""
+    return pair_bound(wq, wk, d)
 
 
-@pytest.mark.parametrize("big_weight", [False, True])
-def test_dense_running_max_rescale(big_weight):
+@pytest.mark.parametrize("weights", ["standard", "shifted", "online"])
+def test_dense_running_max_rescale(weights):
     """Queries 0..63 meet keys aligned with them (logit ~ sqrt(96) ~ 9.4) only in the second tile,
-    well above every earlier block max (~3).  With one large query weight (channel pair 0) the logit
-    bound exceeds the static-shift limit, the running-max kernel runs, and the block sums of p pass 2^8
-    there, so its max must move, rescaling O and the row sum.  With standard weights the static
-    kernel runs the same case."""
+    well above every earlier block max (~3).  With one query weight (channel 0) raised to a logit bound of
+    90, past the static limit, the running-max kernel runs, and the block sums of p pass 2^8 there, so its
+    max must move, rescaling O and the row sum.  With standard weights the static kernel runs the same
+    case, and with that channel at 4 (bound between 48 and 80) the static kernel with its constant shift."""
     wl = custom_workload(1, 5, 40, 2, seed=41, smooth=False)        # N = 200: keys 136..199 aligned
     x = make_inputs(wl)
-    if big_weight:
+    N = wl.N
+    if weights == "shifted":
         x.wq = x.wq.copy()
         x.wq[0] = 4.0
-    assert (static_shift_bound(x.wq, x.wk) > 48) == big_weight
-    N = wl.N
+        assert UNSHIFTED_LIMIT < static_shift_bound(x.wq, x.wk) <= STATIC_LIMIT
     for hd in range(wl.heads):
         x.k.bits[N - 64:, hd, :] = aligned_keys(x, wl, np.arange(64), np.arange(N - 64, N), hd)
+    if weights == "online":
+        # raised after the keys are aligned (with the standard weights): the late logits stay near 9 instead of
+        # growing with the raised channel, where bf16 q^ and k^ would carry about 2.5e-2 of error into O
+        x.wq = spike_to_bound(x.wq, x.wk, 96, 0)
+        assert static_shift_bound(x.wq, x.wk) > STATIC_LIMIT
+    elif weights == "standard":
+        assert static_shift_bound(x.wq, x.wk) <= UNSHIFTED_LIMIT
     L = A.logits(x.q, x.k, x.wq, x.wk, wl.T, wl.H, wl.W, 0, rows=np.arange(64))
     assert np.all(L[np.arange(64), N - 64 + np.arange(64)] - L[:, :N - 64].max(axis=1) > 8 / np.log2(np.e))
     got = as_np(run_dense(x))
     ref = A.attention(x.q, x.k, x.v, x.wq, x.wk, wl.T, wl.H, wl.W)
-    check_close(got, ref, f"dense late max ({'running max' if big_weight else 'static shift'})")
+    check_close(got, ref, f"dense late max ({weights} weights)")
 
 
 def test_dense_deterministic():
@@ -253,19 +261,22 @@ def test_route_then_sparse_pipeline():
     check_close(as_np(o), ref, "route+sparse")
 
 
+@pytest.mark.parametrize("bound", [47.0, 79.0])
 @pytest.mark.parametrize("sparse", [False, True])
-def test_static_rows_whose_logits_are_all_very_negative(sparse):
-    """Every key anti-aligned with every query, with logits about -46 in base 2, on a ragged grid
+def test_static_rows_whose_logits_are_all_very_negative(sparse, bound):
+    """Every key anti-aligned with every query, with logits near -bound in base 2, on a ragged grid
     (500 tokens, so the last KV tile has 12 keys past the grid), under weights that still select the
-    static-shift kernel.  The row sums are then about 500 * 2^-46.  Keys past the grid must be masked out.
-    If they were counted with p = 1 and their count subtracted at the end, the row sum would vanish
-    next to that count in fp32 and O would drop to zero.  q and k put all their energy on the
+    static kernel: at a bound of 47 without a shift (row sums about 500 * 2^-46), at 79 with the shift of
+    31 (p about 2^-109, the low end of the range the shift guarantees normal).  Keys past the grid must be
+    masked out.  If they were counted with p = 1 and their count subtracted at the end, the row sum would
+    vanish next to that count in fp32 and O would drop to zero.  q and k put all their energy on the
     lowest-frequency RoPE pair of each axis, whose rotation over the grid is below 0.01 rad."""
     T, H, W, d = 1, 10, 50, 96
     N = T * H * W
-    c = np.sqrt(47.0 / (np.log2(np.e) * np.sqrt(d) * 1.02))
+    c = np.sqrt(bound / (np.log2(np.e) * np.sqrt(d) * 1.02))
     w = np.full(d, c, dtype=np.float32)
-    assert 46.5 < static_shift_bound(w, w) <= 48
+    edge = UNSHIFTED_LIMIT if bound < UNSHIFTED_LIMIT else STATIC_LIMIT
+    assert bound - 0.5 < static_shift_bound(w, w) <= edge
     x = np.zeros((N, 1, d), dtype=np.float32)
     x[:, 0, [30, 62, 94]] = 1.0
     rng = np.random.default_rng(11)
@@ -285,7 +296,7 @@ def test_static_rows_whose_logits_are_all_very_negative(sparse):
     torch.cuda.synchronize()
     f = lambda b: (b.astype(np.uint32) << 16).view(np.float32)
     L = A.logits(f(qb), f(kb), w, w, T, H, W, 0)
-    assert L.max() * np.log2(np.e) < -45                      # every logit far below zero
+    assert L.max() * np.log2(np.e) < -(bound - 2)             # every logit far below zero
     ref = A.attention(f(qb), f(kb), f(vb), w, w, T, H, W)
     assert np.abs(ref[:, 0] - f(vb)[:, 0].mean(axis=0)).max() < 0.05   # nearly uniform weights
     check_close(as_np(o), ref, f"all logits very negative, {'sparse' if sparse else 'dense'}")

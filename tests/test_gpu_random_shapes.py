@@ -1,9 +1,10 @@
 """GPU parity on seeded random configurations: grid shapes from 1 token up to a few thousand, 1-4 heads,
 head dims 96 and 128, two RoPE bases, and all four attention calls (dense, block-sparse on a random mask,
 router then block-sparse, joint with random positions and Nq != Nkv), each against the fp64 oracle on
-every row.  Cases 16-23 set one random channel of w_q to 4, which takes the pairwise logit bound past
-the static-shift limit, so the same calls run the running-maximum kernels.  Tolerances as everywhere: O within max-abs 2e-2 and relative L2 1e-2,
-masks bit-exact."""
+every row.  Cases 16-23 set one random channel of w_q to 4, which takes the pairwise logit bound past 48
+(the static mode then shifts its exponent by a constant); cases 24-31 raise one random channel of w_q until
+the bound is 90, past the static limit of 80, so the same calls run the running-maximum kernels.  Tolerances
+as everywhere: O within max-abs 2e-2 and relative L2 1e-2, masks bit-exact."""
 import numpy as np
 import pytest
 import torch
@@ -13,12 +14,15 @@ from oracle import attention as A
 from oracle import router as R
 from synth import bf16_bits_to_f32, custom_workload, f32_to_bf16_bits, make_inputs
 
+from bounds import STATIC_LIMIT, UNSHIFTED_LIMIT, pair_bound, spike_to_bound
+
 pytestmark = pytest.mark.gpu
 DEV = torch.device("cuda:0")
 MAX_ABS, REL_L2 = 2e-2, 1e-2
 MODES = ("dense", "sparse", "route_sparse", "joint")
-CASES = 24
-BIG_FROM = 16            # cases from here on: one w_q channel at 4 (running-maximum softmax)
+CASES = 32
+BIG_FROM = 16            # cases 16-23: one w_q channel at 4 (shifted static softmax)
+ONLINE_FROM = 24         # cases 24-31: one w_q channel raised to a bound of 90 (running-maximum softmax)
 
 
 def check_close(got, ref, what):
@@ -34,11 +38,17 @@ def t16(bits):
     return torch.from_numpy(bits.view(np.int16)).to(DEV).view(torch.bfloat16)
 
 
-def pair_bound(wq, wk, d):
-    """log2(e) sqrt(d) max_i u_i v_i with the 2% margin: above 48 the running-maximum kernels run."""
-    u = np.maximum(np.abs(wq[0::2]), np.abs(wq[1::2])).astype(np.float64)
-    v = np.maximum(np.abs(wk[0::2]), np.abs(wk[1::2])).astype(np.float64)
-    return np.log2(np.e) * np.sqrt(d) * float(np.max(u * v)) * 1.02
+def spiked(wq, wk, d, big, online):
+    """w_q with channel `big` at 4 (bound between 48 and 80) or raised to a bound of 90; the kernel the bound
+    selects is asserted."""
+    if online:
+        w = spike_to_bound(wq, wk, d, big)
+        assert pair_bound(w, wk, d) > STATIC_LIMIT
+    else:
+        w = np.array(wq, dtype=np.float32, copy=True)
+        w[big] = 4.0
+        assert UNSHIFTED_LIMIT < pair_bound(w, wk, d) <= STATIC_LIMIT
+    return w
 
 
 def config(i):
@@ -58,7 +68,9 @@ def config(i):
 def test_random_configuration(i):
     rng, mode, d, (T, H, W), heads, theta = config(i)
     big = int(rng.integers(0, d)) if i >= BIG_FROM else None
-    what = f"case {i}: {mode} d={d} grid={T}x{H}x{W} heads={heads} theta={theta:g} big w_q channel {big}"
+    online = i >= ONLINE_FROM
+    what = (f"case {i}: {mode} d={d} grid={T}x{H}x{W} heads={heads} theta={theta:g} big w_q channel {big}"
+            + (" (running max)" if online else ""))
     print(what, flush=True)
     if mode == "joint":
         nq, nk, max_pos = int(rng.integers(1, 600)), int(rng.integers(1, 1500)), int(rng.integers(1, 65))
@@ -70,8 +82,9 @@ def test_random_configuration(i):
         wq = (1 + 0.1 * rng.standard_normal(d)).astype(np.float32)
         wk = (1 + 0.1 * rng.standard_normal(d)).astype(np.float32)
         if big is not None:
-            wq[big] = 4.0
-        assert (pair_bound(wq, wk, d) > 48) == (big is not None)
+            wq = spiked(wq, wk, d, big, online)
+        else:
+            assert pair_bound(wq, wk, d) <= UNSHIFTED_LIMIT
         o = dit.dit_attn_joint(t16(q), t16(k), t16(v), torch.from_numpy(wq).to(DEV), torch.from_numpy(wk).to(DEV),
                                torch.from_numpy(qp).to(DEV), torch.from_numpy(kp).to(DEV), max_pos, theta)
         torch.cuda.synchronize()
@@ -82,9 +95,9 @@ def test_random_configuration(i):
     wl = custom_workload(T, H, W, heads, seed=6000 + i, head_dim=d, theta=theta)
     x = make_inputs(wl)
     if big is not None:
-        x.wq = x.wq.copy()
-        x.wq[big] = 4.0
-    assert (pair_bound(x.wq, x.wk, d) > 48) == (big is not None)
+        x.wq = spiked(x.wq, x.wk, d, big, online)
+    else:
+        assert pair_bound(x.wq, x.wk, d) <= UNSHIFTED_LIMIT
     q, k, v = t16(x.q.bits), t16(x.k.bits), t16(x.v.bits)
     wq, wk = torch.from_numpy(x.wq).to(DEV), torch.from_numpy(x.wk).to(DEV)
     g = (T, H, W)

@@ -15,6 +15,8 @@ from oracle import attention as A
 from oracle import router as R
 from synth import custom_workload, make_inputs
 
+from bounds import STATIC_LIMIT, pair_bound, spike_to_bound
+
 pytestmark = pytest.mark.gpu
 DEV = torch.device("cuda:0")
 MAX_ABS, REL_L2 = 2e-2, 1e-2
@@ -100,12 +102,12 @@ def test_consecutive_tiles_above_4096_blocks():
 
 @pytest.mark.parametrize("name", ["s4", "s4_128"])
 def test_block_sparse_online_softmax_weights(name):
-    """Norm weights whose logit bound exceeds the static-shift limit: the running-max kernel runs on the
+    """Norm weights whose logit bound (90) exceeds the static limit: the running-max kernel runs on the
     grouped tiles (ragged last block included), router mask from the oracle."""
     x = make_inputs(name)
     wl = x.workload
-    wq = x.wq.copy()
-    wq[5] = 4.0
+    wq = spike_to_bound(x.wq, x.wk, wl.head_dim, 5)
+    assert pair_bound(wq, x.wk, wl.head_dim) > STATIC_LIMIT
     mask = R.route_mask(x.q, x.k, wq, x.wk, wl.T, wl.H, wl.W, 0.75, wl.theta, wl.eps)
     q, k, v, _, wk = upload(x)
     print(f"case sparse online {name}", flush=True)

@@ -44,7 +44,7 @@ CASES = [
 ]
 
 
-@pytest.mark.parametrize("d,scale,big,bheads,small,sheads", CASES, ids=["d96_static", "d128_online"])
+@pytest.mark.parametrize("d,scale,big,bheads,small,sheads", CASES, ids=["d96", "d128_scaled_weights"])
 def test_noalloc_equals_dense_on_two_calls_in_a_row(d, scale, big, bheads, small, sheads):
     limit = dit.NOALLOC_SCRATCH_BYTES
     assert scratch_need(*big, bheads, d) <= limit < scratch_need(*big, bheads, d) + TILE_BYTES[d]
