@@ -314,14 +314,15 @@ __device__ __forceinline__ void load_q(const AttnArgs& a, int head, int qt, int 
   }
 }
 
-// S^T for key sub-block kb (32 keys) against the wave's QB query blocks: KS K^ fragments, KS*QB MFMAs.
+// S^T - m for key sub-block kb (32 keys) against the wave's QB query blocks: KS K^ fragments, KS*QB MFMAs,
+// the first of each query block accumulating onto negm[qb] (every element -m of the lane's query).
 // QM: bit qb set = query block qb takes part (block-sparse tiles kept by only some of a wave's blocks).
 template <int D, int QB, int QM = (1 << QB) - 1>
-__device__ __forceinline__ void qk_block(const uint16_t* T_, int kb, int lane,
-                                         const bf16x8 (&qf)[QB][Head<D>::KS], f32x16 (&S)[QB]) {
+__device__ __forceinline__ void qk_block(const uint16_t* T_, int kb, int lane, const bf16x8 (&qf)[QB][Head<D>::KS],
+                                         const f32x16 (&negm)[QB], f32x16 (&S)[QB]) {
   constexpr int KS = Head<D>::KS;
 #pragma unroll
-  for (int qb = 0; qb < QB; ++qb) S[qb] = f32x16{};
+  for (int qb = 0; qb < QB; ++qb) S[qb] = negm[qb];
 #pragma unroll
   for (int ks = 0; ks < KS; ++ks) {
     const bf16x8 ka = *(const bf16x8*)(T_ + (kb * KS + ks) * kFrag + lane * 8);
@@ -330,6 +331,11 @@ __device__ __forceinline__ void qk_block(const uint16_t* T_, int kb, int lane,
       if (((QM >> qb) & 1) != 0)
         S[qb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka, qf[qb][ks], S[qb], 0, 0, 0);
   }
+  // A second reader of each -m block beside its MFMA: with the MFMA as the only one the compiler accumulates in
+  // place and copies the block into S every sub-block (16 register moves) instead of reading it as a separate
+  // accumulator input.
+#pragma unroll
+  for (int qb = 0; qb < QB; ++qb) asm volatile("" ::"v"(negm[qb]));
 }
 
 // O^T += V^T P^T for key sub-block kb: 2*DB V^T fragments, 2*DB*QB MFMAs.
@@ -382,39 +388,48 @@ __device__ __forceinline__ void mask_past_grid(f32x16 (&S)[QB], int key0, int N,
   }
 }
 
-// Online (running-max) softmax of one sub-block; keys >= N get probability 0.
+// Online (running-max) softmax of one sub-block.  S holds the logits less the lane's running max m (the
+// accumulator input of the sub-block's first S MFMA was -m), so p = exp2(S) needs no subtraction; keys >= N get
+// probability 0.  Every p is at most its lane's block sum, so while every sum of the wave stays within
+// kSumLimit no p exceeds it and m needs no update.  The block max is only computed when some sum of the wave is
+// larger, infinite or NaN, or some lane has no max yet (mset false: before its first block with a live key):
+// then m moves up to the block max (to it, for a first block), O and l are rescaled, p is redone with the extra
+// subtraction and -m is written to negm for the next sub-blocks.
+// The running max lives only in negm (m = -negm[qb][0]), which gives the block a use besides the MFMA: with
+// the MFMA as its only reader the compiler accumulates in place and copies the block into S every sub-block.
 template <int DB, int QB, int QM = (1 << QB) - 1>
 __device__ __forceinline__ void softmax_online(f32x16 (&S)[QB], bool ragged, int key0, int N, int lane,
-                                               float (&m)[QB], float (&l)[QB], f32x16 (&acc)[QB][DB],
-                                               bf16x8 (&P)[QB][2]) {
+                                               bool (&mset)[QB], f32x16 (&negm)[QB], float (&l)[QB],
+                                               f32x16 (&acc)[QB][DB], bf16x8 (&P)[QB][2]) {
   if (ragged) mask_past_grid<QB>(S, key0, N, lane);
 #pragma unroll
   for (int qb = 0; qb < QB; ++qb) {
     if (((QM >> qb) & 1) == 0) continue;
-    // p = exp2(S - m) with the current running max.  Every p is at most its lane's block sum, so while
-    // every sum stays within kSumLimit no p exceeds it and m needs no update: the block max is only
-    // computed when some sum of the wave is larger, infinite or NaN (the first block, where m is still
-    // the -1e30 start, always is).  Then m moves to the block max, O and l are rescaled and p is redone.
     float p[16];
 #pragma unroll
-    for (int i = 0; i < 16; ++i) p[i] = __builtin_amdgcn_exp2f(S[qb][i] - m[qb]);
+    for (int i = 0; i < 16; ++i) p[i] = __builtin_amdgcn_exp2f(S[qb][i]);
     float lb = 0.f;
     pack_probs(p, lb, P[qb]);
-    if (__builtin_amdgcn_ballot_w64(!(lb <= kSumLimit))) {
+    if (__builtin_amdgcn_ballot_w64(!mset[qb] || !(lb <= kSumLimit))) {
       float mx = S[qb][0];
 #pragma unroll
       for (int i = 1; i < 16; ++i) mx = fmaxf(mx, S[qb][i]);
       mx = pair_max(mx);
-      const float mn = fmaxf(m[qb], mx);
-      const float alpha = __builtin_amdgcn_exp2f(m[qb] - mn);
+      // raise of m: up to the block max (to it, for a lane without a max yet); none for a block of masked keys
+      const bool live = mx > -INFINITY;
+      const float d = live ? (mset[qb] ? fmaxf(mx, 0.f) : mx) : 0.f;
+      const float alpha = __builtin_amdgcn_exp2f(-d);
       l[qb] *= alpha;
 #pragma unroll
       for (int db = 0; db < DB; ++db) acc[qb][db] *= alpha;
-      m[qb] = mn;
+      const float mnew = d - negm[qb][0];
+      mset[qb] = mset[qb] || live;
 #pragma unroll
-      for (int i = 0; i < 16; ++i) p[i] = __builtin_amdgcn_exp2f(S[qb][i] - m[qb]);
+      for (int i = 0; i < 16; ++i) p[i] = __builtin_amdgcn_exp2f(S[qb][i] - d);
       lb = 0.f;
       pack_probs(p, lb, P[qb]);
+#pragma unroll
+      for (int i = 0; i < 16; ++i) negm[qb][i] = -mnew;
     }
     l[qb] += lb;
   }
@@ -624,8 +639,8 @@ __device__ __forceinline__ void qk_block_pre(const uint16_t* T_, int kb, int lan
 
 template <int D, int QB, int QM, int MODE>
 __device__ __forceinline__ void tile_body(const uint16_t* T_, int lane, const bf16x8 (&qf)[QB][Head<D>::KS],
-                                          f32x16 (&acc)[QB][Head<D>::DB], float (&m)[QB], float (&l)[QB],
-                                          const f32x16& negc, bool ragged, int key0, int N) {
+                                          f32x16 (&acc)[QB][Head<D>::DB], bool (&mset)[QB], f32x16 (&negm)[QB],
+                                          float (&l)[QB], const f32x16& negc, bool ragged, int key0, int N) {
   constexpr int KS = Head<D>::KS;
   if constexpr (MODE == kStatic) {
     // The first two K^ fragments of each sub-block are read while the previous sub-block's S MFMAs
@@ -654,9 +669,9 @@ __device__ __forceinline__ void tile_body(const uint16_t* T_, int lane, const bf
 #pragma unroll 1
     for (int kb = 0; kb < BK / 32; ++kb) {
       f32x16 S[QB];
-      qk_block<D, QB, QM>(T_, kb, lane, qf, S);
+      qk_block<D, QB, QM>(T_, kb, lane, qf, negm, S);
       bf16x8 P[QB][2];
-      softmax_online<Head<D>::DB, QB, QM>(S, ragged, key0 + kb * 32, N, lane, m, l, acc, P);
+      softmax_online<Head<D>::DB, QB, QM>(S, ragged, key0 + kb * 32, N, lane, mset, negm, l, acc, P);
       pv_block<D, QB, QM>(T_, kb, lane, P, acc);
     }
   }
@@ -691,10 +706,15 @@ __device__ __forceinline__ void attn_kernel_body(const AttnArgs& a, uint16_t* sK
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) asm volatile("" ::"v"(qf[qb][ks]));
   f32x16 acc[QB][DB];
-  float m[QB], l[QB];
+  // Online mode: -m, the running max of the lane's query (0 and not yet set before its first block with a
+  // live key), in every element of negm, the accumulator input of each sub-block's first S MFMA.
+  float l[QB];
+  bool mset[QB];
+  f32x16 negm[QB];
 #pragma unroll
   for (int qb = 0; qb < QB; ++qb) {
-    m[qb] = -1e30f;
+    mset[qb] = false;
+    negm[qb] = f32x16{};
     l[qb] = 0.f;
 #pragma unroll
     for (int db = 0; db < DB; ++db) acc[qb][db] = f32x16{};
@@ -729,15 +749,16 @@ __device__ __forceinline__ void attn_kernel_body(const AttnArgs& a, uint16_t* sK
     const bool ragged = (tile + 1) * BK > N;
     if constexpr (SPARSE && QB == 2) {
       if (qm == 3)
-        tile_body<D, QB, 3, MODE>(T_, lane, qf, acc, m, l, negc, ragged, tile * BK, N);
+        tile_body<D, QB, 3, MODE>(T_, lane, qf, acc, mset, negm, l, negc, ragged, tile * BK, N);
       else if (qm == 1)
-        tile_body<D, QB, 1, MODE>(T_, lane, qf, acc, m, l, negc, ragged, tile * BK, N);
+        tile_body<D, QB, 1, MODE>(T_, lane, qf, acc, mset, negm, l, negc, ragged, tile * BK, N);
       else if (qm == 2)
-        tile_body<D, QB, 2, MODE>(T_, lane, qf, acc, m, l, negc, ragged, tile * BK, N);
+        tile_body<D, QB, 2, MODE>(T_, lane, qf, acc, mset, negm, l, negc, ragged, tile * BK, N);
     } else if constexpr (SPARSE) {
-      if (qm != 0) tile_body<D, QB, (1 << QB) - 1, MODE>(T_, lane, qf, acc, m, l, negc, ragged, tile * BK, N);
+      if (qm != 0) tile_body<D, QB, (1 << QB) - 1, MODE>(T_, lane, qf, acc, mset, negm, l, negc, ragged, tile * BK, N);
     } else {
-      tile_body<D, QB, (1 << QB) - 1, MODE>(T_, lane, qf, acc, m, l, negc, ragged, tile * BK, N);
+      tile_body<D, QB, (1 << QB) - 1, MODE>(T_, lane, qf, acc, mset, negm, l, negc, ragged, tile * BK,
+                                            N);
     }
     tile_barrier();
     e_cur = e_nxt;
