@@ -93,11 +93,12 @@ def log(msg):
 
 
 class ClockSampler:
-    """Samples the GPU's graphics clock while the timed steps run, in a background thread: the mean of the eight
-    XCDs' current clocks from amdsmi's GPU metrics, else the current level of pp_dpm_sclk in sysfs.  Reports the
-    mean, min and max over the samples (MHz), or None where neither source is readable."""
+    """Samples the GPU's graphics clock while the timed steps run, in a background thread: the current level of
+    pp_dpm_sclk in sysfs (the power firmware's clock, refreshed every few milliseconds), else the mean of the
+    XCDs' current clocks from amdsmi's GPU metrics (refreshed about once a second).  Reports the mean, median,
+    min and max over the samples (MHz), or None where neither source is readable."""
 
-    def __init__(self, period_s: float = 0.02):
+    def __init__(self, period_s: float = 0.01):
         import threading
         self.period = period_s
         self.samples = []
@@ -107,6 +108,19 @@ class ClockSampler:
         self._read = self._open()
 
     def _open(self):
+        import glob
+        for path in sorted(glob.glob("/sys/class/drm/card*/device/pp_dpm_sclk")):
+            def read(path=path):
+                for line in open(path).read().splitlines():
+                    if line.rstrip().endswith("*"):
+                        return float(re.findall(r"(\d+)\s*[Mm]hz", line)[0])
+                return None
+            try:
+                if read() is not None:
+                    self.source = f"sysfs {path} (current level)"
+                    return read
+            except Exception:
+                continue
         try:
             import amdsmi
             amdsmi.amdsmi_init()
@@ -121,19 +135,6 @@ class ClockSampler:
                 return read
         except Exception:
             pass
-        import glob
-        for path in sorted(glob.glob("/sys/class/drm/card*/device/pp_dpm_sclk")):
-            def read(path=path):
-                for line in open(path).read().splitlines():
-                    if line.rstrip().endswith("*"):
-                        return float(re.findall(r"(\d+)\s*[Mm]hz", line)[0])
-                return None
-            try:
-                if read() is not None:
-                    self.source = f"sysfs {path} (current level)"
-                    return read
-            except Exception:
-                continue
         return None
 
     def _run(self):

@@ -576,28 +576,30 @@ __global__ void __launch_bounds__(256) kv_prep_kernel(AttnArgs a) {
   }
 }
 
-// One 16-byte-per-lane global -> LDS copy issued as inline assembly (lane l writes LDS bytes
-// [dst + 16 l, dst + 16 l + 16)).  With the builtin, the compiler cannot order the copy against later LDS
+// One 16-byte-per-lane global -> LDS copy issued as inline assembly: lane l reads the 16 bytes at
+// src + voff_l (src a wave-uniform address in scalar registers, voff_l = 16 l) and writes LDS bytes
+// [dst + 16 l, dst + 16 l + 16).  With the builtin, the compiler cannot order the copy against later LDS
 // reads and waits for every outstanding read (lgkmcnt(0)) before each use; the assembly form has no
 // register result, the copy only counts against vmcnt (waited for explicitly at the tile barrier), and the
-// reads of the current stage get graded waits.  The memory clobber keeps LDS accesses on their side.
-__device__ __forceinline__ void lds_copy16(const void* src, __attribute__((address_space(3))) void* lds_dst) {
+// reads of the current stage get graded waits.  The memory clobber keeps LDS accesses on their side.  Both
+// addresses are wave-uniform, so forming them takes scalar instructions only.
+__device__ __forceinline__ void lds_copy16(const void* src, uint32_t voff, __attribute__((address_space(3))) void* lds_dst) {
   const uint32_t base = (uint32_t)(uintptr_t)lds_dst;
-  asm volatile("global_load_lds_dwordx4 %0, off" ::"v"(src), "{m0}"(base) : "memory");
+  asm volatile("global_load_lds_dwordx4 %0, %1" ::"v"(voff), "s"(src), "{m0}"(base) : "memory");
 }
 
 // This wave's share (fragments FPW*w .. FPW*w + FPW-1, FPW = FRAGS / 8) of one tile's fragment image,
 // copied global -> LDS without passing through registers: lane l of each copy moves the 16 bytes of lane
-// slot l.
+// slot l.  src (the tile's image), wave and dst are wave-uniform; voff = 16 * lane.
 template <int D>
-__device__ __forceinline__ void dma_tile(const uint16_t* src, int wave, int lane, uint16_t* dst) {
+__device__ __forceinline__ void dma_tile(const uint16_t* src, int wave, uint32_t voff, uint16_t* dst) {
   typedef __attribute__((address_space(3))) void lds_void;
   constexpr int FPW = Head<D>::FRAGS / Head<D>::NW;
   static_assert(FPW * Head<D>::NW == Head<D>::FRAGS, "fragments per wave");
 #pragma unroll
   for (int c = 0; c < FPW; ++c) {
     const int f = FPW * wave + c;
-    lds_copy16((const void*)(src + f * kFrag + lane * 8), (lds_void*)(dst + f * kFrag));
+    lds_copy16((const void*)(src + f * kFrag), voff, (lds_void*)(dst + f * kFrag));
   }
 }
 
@@ -686,6 +688,10 @@ __device__ __forceinline__ void attn_kernel_body(const AttnArgs& a, uint16_t* sK
   TileIter ti;
   if (!tile_iter<SPARSE>(a, ti)) return;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  // A scalar copy of the wave index for the tile copies, whose addresses are then scalar arithmetic.  (Used
+  // everywhere, it costs the block-sparse kernel at head dim 96 register spills.)
+  const int wave_s = __builtin_amdgcn_readfirstlane(wave);
+  const uint32_t voff = 16u * (uint32_t)lane;
   float shift;
   if (static_bound_holds<D>(a, lane, shift) != (MODE == kStatic)) return;   // the other kernel takes these weights
   f32x16 negc;
@@ -696,7 +702,7 @@ __device__ __forceinline__ void attn_kernel_body(const AttnArgs& a, uint16_t* sK
 #pragma unroll
   for (int qb = 0; qb < QB; ++qb) rbit[qb] = router_block<QB, SPARSE, Head<D>::NW>(wave, qb);
   const uint16_t* img = a.kvf + (size_t)ti.head * a.nb * TILE;
-  if (nt > 0) dma_tile<D>(img + (size_t)ti.tile(0, SPARSE) * TILE, wave, lane, sKV);
+  if (nt > 0) dma_tile<D>(img + (size_t)__builtin_amdgcn_readfirstlane(ti.tile(0, SPARSE)) * TILE, wave_s, voff, sKV);
   bf16x8 qf[QB][KS];
   load_q<D, QB, BQ, SPARSE>(a, ti.head, ti.qt, wave, lane, qf);
   // Finish Q here: left free, the compiler sinks the norm and rotation below the first tile barrier,
@@ -724,11 +730,13 @@ __device__ __forceinline__ void attn_kernel_body(const AttnArgs& a, uint16_t* sK
   // vmcnt(0) waits for them, so no visit stalls on a list read before it can start the next copy and its
   // own MFMAs.  Tile indices and flags come from separate arrays: a copy address is formed from a plain
   // tile index, with no field to mask off.
+  // List entries are the same in every lane; the loaded ones (in flight: vector registers) are made scalar one
+  // visit before their use, which keeps the copy addressing and the activity mask scalar.
   int e_cur = 0, e_nxt = 0, f_cur = 0, f_nxt = 0;
   if constexpr (SPARSE) {
-    e_cur = nt > 0 ? ti.lst[0] : 0;
+    e_cur = nt > 0 ? __builtin_amdgcn_readfirstlane(ti.lst[0]) : 0;
     e_nxt = nt > 1 ? ti.lst[1] : 0;
-    f_cur = nt > 0 ? ti.flg[0] : 0;
+    f_cur = nt > 0 ? __builtin_amdgcn_readfirstlane(ti.flg[0]) : 0;
     f_nxt = nt > 1 ? ti.flg[1] : 0;
   }
   tile_barrier();
@@ -737,15 +745,17 @@ __device__ __forceinline__ void attn_kernel_body(const AttnArgs& a, uint16_t* sK
     if constexpr (SPARSE) {
       e_nn = it + 2 < nt ? ti.lst[it + 2] : 0;
       f_nn = it + 2 < nt ? ti.flg[it + 2] : 0;
+      e_nxt = __builtin_amdgcn_readfirstlane(e_nxt);   // loaded a visit ago
+      f_nxt = __builtin_amdgcn_readfirstlane(f_nxt);
     }
     const int st = it & 1, tile = SPARSE ? e_cur : it;
     if (it + 1 < nt)
-      dma_tile<D>(img + (size_t)(SPARSE ? e_nxt : it + 1) * TILE, wave, lane, sKV + (st ^ 1) * TILE);
+      dma_tile<D>(img + (size_t)(SPARSE ? e_nxt : it + 1) * TILE, wave_s, voff, sKV + (st ^ 1) * TILE);
     const int flags = SPARSE ? f_cur : 0xff;
     int qm = 0;
 #pragma unroll
     for (int qb = 0; qb < QB; ++qb) qm |= ((flags >> rbit[qb]) & 1) << qb;
-    const uint16_t* T_ = sKV + st * TILE;
+    const uint16_t* T_ = sKV + (st != 0 ? TILE : 0);     // a select, not a multiply by the stage
     const bool ragged = (tile + 1) * BK > N;
     if constexpr (SPARSE && QB == 2) {
       if (qm == 3)
