@@ -639,8 +639,17 @@ __device__ __forceinline__ void qk_block_pre(const uint16_t* T_, int kb, int lan
   }
 }
 
+// Issue priority of the younger wave of each SIMD (waves 4-7 share SIMDs with waves 0-3, which the issue
+// arbiter favours) raised for a tile's last sub-block, so it catches up with its partner before the tile
+// barrier instead of finishing the tile alone.  Reset after the barrier.  Dense only: measured 0.9% faster on
+// the dense layer and 0.7% slower on the block-sparse one.
+__device__ __forceinline__ void raise_younger_wave(int kb, int wave) {
+  if (kb == BK / 32 - 1 && wave >= 4) __builtin_amdgcn_s_setprio(1);
+}
+
 template <int D, int QB, int QM, int MODE>
-__device__ __forceinline__ void tile_body(const uint16_t* T_, int lane, const bf16x8 (&qf)[QB][Head<D>::KS],
+__device__ __forceinline__ void tile_body(const uint16_t* T_, int lane, int wave, bool balance,
+                                          const bf16x8 (&qf)[QB][Head<D>::KS],
                                           f32x16 (&acc)[QB][Head<D>::DB], bool (&mset)[QB], f32x16 (&negm)[QB],
                                           float (&l)[QB], const f32x16& negc, bool ragged, int key0, int N) {
   constexpr int KS = Head<D>::KS;
@@ -651,8 +660,8 @@ __device__ __forceinline__ void tile_body(const uint16_t* T_, int lane, const bf
     bf16x8 kp[2];
     kp[0] = *(const bf16x8*)(T_ + 0 * kFrag + lane * 8);
     kp[1] = *(const bf16x8*)(T_ + 1 * kFrag + lane * 8);
-#pragma unroll 1
-    for (int kb = 0; kb < BK / 32; ++kb) {
+    auto sub_block = [&](int kb) {
+      if (balance) raise_younger_wave(kb, wave);
       f32x16 S[QB];
       qk_block_pre<D, QB, QM>(T_, kb, lane, qf, kp, negc, S);
       const int nk = kb + 1 < BK / 32 ? kb + 1 : kb;   // the last sub-block re-reads its own (unused)
@@ -666,10 +675,21 @@ __device__ __forceinline__ void tile_body(const uint16_t* T_, int lane, const bf
       softmax_static<QB, QM>(S, l, P);
       pv_block<D, QB, QM>(T_, kb, lane, P, acc);
       asm volatile("" ::"v"(kp[0]), "v"(kp[1]));   // keeps the reads where they are issued
+    };
+    if (balance) {
+      // Dense: the four sub-blocks unrolled (fragment offsets become immediates, no loop bookkeeping):
+      // measured 0.9% faster on the dense layer.  The block-sparse variants keep the loop, whose unrolled
+      // form spills registers at the loop boundary.
+#pragma unroll
+      for (int kb = 0; kb < BK / 32; ++kb) sub_block(kb);
+    } else {
+#pragma unroll 1
+      for (int kb = 0; kb < BK / 32; ++kb) sub_block(kb);
     }
   } else {
 #pragma unroll 1
     for (int kb = 0; kb < BK / 32; ++kb) {
+      if (balance) raise_younger_wave(kb, wave);
       f32x16 S[QB];
       qk_block<D, QB, QM>(T_, kb, lane, qf, negm, S);
       bf16x8 P[QB][2];
@@ -759,18 +779,19 @@ __device__ __forceinline__ void attn_kernel_body(const AttnArgs& a, uint16_t* sK
     const bool ragged = (tile + 1) * BK > N;
     if constexpr (SPARSE && QB == 2) {
       if (qm == 3)
-        tile_body<D, QB, 3, MODE>(T_, lane, qf, acc, mset, negm, l, negc, ragged, tile * BK, N);
+        tile_body<D, QB, 3, MODE>(T_, lane, wave, false, qf, acc, mset, negm, l, negc, ragged, tile * BK, N);
       else if (qm == 1)
-        tile_body<D, QB, 1, MODE>(T_, lane, qf, acc, mset, negm, l, negc, ragged, tile * BK, N);
+        tile_body<D, QB, 1, MODE>(T_, lane, wave, false, qf, acc, mset, negm, l, negc, ragged, tile * BK, N);
       else if (qm == 2)
-        tile_body<D, QB, 2, MODE>(T_, lane, qf, acc, mset, negm, l, negc, ragged, tile * BK, N);
+        tile_body<D, QB, 2, MODE>(T_, lane, wave, false, qf, acc, mset, negm, l, negc, ragged, tile * BK, N);
     } else if constexpr (SPARSE) {
-      if (qm != 0) tile_body<D, QB, (1 << QB) - 1, MODE>(T_, lane, qf, acc, mset, negm, l, negc, ragged, tile * BK, N);
+      if (qm != 0) tile_body<D, QB, (1 << QB) - 1, MODE>(T_, lane, wave, false, qf, acc, mset, negm, l, negc, ragged, tile * BK, N);
     } else {
-      tile_body<D, QB, (1 << QB) - 1, MODE>(T_, lane, qf, acc, mset, negm, l, negc, ragged, tile * BK,
+      tile_body<D, QB, (1 << QB) - 1, MODE>(T_, lane, wave, true, qf, acc, mset, negm, l, negc, ragged, tile * BK,
                                             N);
     }
     tile_barrier();
+    if constexpr (!SPARSE) __builtin_amdgcn_s_setprio(0);
     e_cur = e_nxt;
     e_nxt = e_nn;
     f_cur = f_nxt;
