@@ -76,6 +76,7 @@ struct Layout {
   size_t list_len;   // [heads][nqt] i32
   size_t perm;       // [heads][nqt][query tile / 128] i32 router block per query-tile slot
   size_t bits;       // [heads][nb][schedule_words(nb)] u64 packed mask rows
+  size_t partial;    // dense tail pieces: fp32 partial results (dit::tail_partial_area)
   size_t total;
 };
 
@@ -100,7 +101,12 @@ Layout make_layout(const Shape& s) {
   L.list_len = L.list_flags + flag_bytes;
   L.perm = L.list_len + len_bytes;
   L.bits = L.perm + perm_bytes;
-  L.total = base + std::max(pool_bytes + score_bytes, list_bytes + flag_bytes + len_bytes + perm_bytes + bits_bytes);
+  // Dense calls use neither the router's nor the block-sparse schedule's share: their tail partials
+  // (if the call splits its last round) share that space.
+  L.partial = base;
+  const size_t partial_bytes = dit::tail_partial_area(dit::tail_plan(s.heads * s.nqt, (int)s.N), s.d);
+  L.total = base + std::max({pool_bytes + score_bytes, list_bytes + flag_bytes + len_bytes + perm_bytes + bits_bytes,
+                             partial_bytes});
   return L;
 }
 
@@ -282,7 +288,12 @@ dit::AttnArgs attn_args(const Shape& s, const void* q, const void* k, const void
   a.eps = eps;
   a.nqt = s.nqt;
   a.total = s.heads * s.nqt;
-  a.per_xcd = (a.total + 7) / 8;
+  const dit::TailPlan tp = dit::tail_plan(a.total, a.nk);
+  a.per_xcd = tp.per_xcd;
+  a.main_per_xcd = tp.main_per_xcd;
+  a.tail_rem = tp.rem;
+  a.tail_pieces = tp.pieces;
+  a.partial = (float*)((char*)ws + L.partial);
   a.order = g_launch_order.load(std::memory_order_relaxed);
   a.nb = s.nb;
   return a;
@@ -302,8 +313,9 @@ struct JointShape {
 };
 
 struct JointLayout {
-  size_t tab;   // RoPE table [sections * max_pos][rope_row_floats(d)] f32
-  size_t kvf;   // K^ / V^T fragment images [heads][nb] x tile_image_bytes(d)
+  size_t tab;       // RoPE table [sections * max_pos][rope_row_floats(d)] f32
+  size_t kvf;       // K^ / V^T fragment images [heads][nb] x tile_image_bytes(d)
+  size_t partial;   // tail partial results (dit::tail_partial_area)
   size_t total;
 };
 
@@ -311,7 +323,8 @@ JointLayout make_joint_layout(const JointShape& j) {
   JointLayout L{};
   L.tab = 0;
   L.kvf = align256((size_t)j.sections * j.max_pos * dit::rope_row_floats(j.d) * sizeof(float));
-  L.total = L.kvf + (size_t)j.heads * j.nb * dit::tile_image_bytes(j.d);
+  L.partial = align256(L.kvf + (size_t)j.heads * j.nb * dit::tile_image_bytes(j.d));
+  L.total = L.partial + dit::tail_partial_area(dit::tail_plan(j.heads * j.nqt, j.nk), j.d);
   return L;
 }
 
@@ -552,7 +565,12 @@ dit_status dit_attn_joint(const void* q, const void* k, const void* v, const flo
     a.eps = eps;
     a.nqt = j.nqt;
     a.total = heads * j.nqt;
-    a.per_xcd = (a.total + 7) / 8;
+    const dit::TailPlan tp = dit::tail_plan(a.total, nk);
+    a.per_xcd = tp.per_xcd;
+    a.main_per_xcd = tp.main_per_xcd;
+    a.tail_rem = tp.rem;
+    a.tail_pieces = tp.pieces;
+    a.partial = (float*)((char*)workspace + L.partial);
     a.order = g_launch_order.load(std::memory_order_relaxed);
     a.nb = j.nb;
     const hipError_t e = dit::launch_attn_dense(a, stream);
@@ -610,9 +628,10 @@ dit_status dit_attn_dense_noalloc(const void* q, const void* k, const void* v, c
     if ((st = check_common(q, k, wq, wk, rope_theta, eps)) != DIT_OK) return st;
     if (!v || !o) return fail(DIT_ERR_INVALID_ARG, "null v or o");
     if (!aligned16(v) || !aligned16(o)) return fail(DIT_ERR_INVALID_ARG, "v and o must be 16-byte aligned");
-    // The dense part of the workspace layout: RoPE table, then the fragment images.
+    // The dense part of the workspace layout: RoPE table, the fragment images, then the tail partials of a
+    // call that splits its last round.
     const Layout L = make_layout(s);
-    const size_t need = L.kvf + (size_t)s.heads * s.nb * dit::tile_image_bytes(s.d);
+    const size_t need = L.partial + dit::tail_partial_area(dit::tail_plan(s.heads * s.nqt, (int)s.N), s.d);
     if (need > kStaticScratchBytes)
       return fail(DIT_ERR_UNSUPPORTED,
                   "needs %zu bytes of scratch (heads x ceil(N/128) tiles of %zu bytes plus the RoPE table); the "

@@ -474,24 +474,80 @@ __device__ __forceinline__ void store_o(const AttnArgs& a, int head, int qt, int
   }
 }
 
+// Partial result of a tail piece: per wave, query block and lane, its DB x 16 accumulators, its row sum
+// and its running maximum (-inf before any key; 0 in the static mode, whose constant shift is the same for
+// every piece), element-major so that each store is coalesced over the lanes.
+template <int D>
+constexpr int kPartialElems = Head<D>::DB * 16 + 2;
+
+template <int D>
+__device__ __forceinline__ void store_partial(const AttnArgs& a, int slot, int wave, int lane,
+                                              const f32x16 (&acc)[Head<D>::QB][Head<D>::DB],
+                                              const float (&l)[Head<D>::QB], const f32x16 (&negm)[Head<D>::QB],
+                                              const bool (&mset)[Head<D>::QB], bool online) {
+  constexpr int QB = Head<D>::QB, DB = Head<D>::DB, NW = Head<D>::NW, E = kPartialElems<D>;
+#pragma unroll
+  for (int qb = 0; qb < QB; ++qb) {
+    float* dst = a.partial + (((size_t)slot * NW + wave) * QB + qb) * E * 64 + lane;
+#pragma unroll
+    for (int db = 0; db < DB; ++db)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) dst[(db * 16 + i) * 64] = acc[qb][db][i];
+    dst[(E - 2) * 64] = l[qb];
+    dst[(E - 1) * 64] = online ? (mset[qb] ? -negm[qb][0] : -INFINITY) : 0.f;
+  }
+}
+
 // Shared setup of both kernels: workgroup -> (head, query tile) with the XCD-aware order, tile list.
 struct TileIter {
   int head, qt, ntiles;
+  int k0;                       // dense: first KV tile (a tail piece starts inside the key range)
+  int slot;                     // tail piece: index of its partial result
   const int* lst;               // block-sparse: visited KV tiles (plain indices below nb)
   const unsigned char* flg;     // block-sparse: slots of the query tile that keep each visited tile
-  __device__ __forceinline__ int tile(int it, bool sparse) const { return sparse ? lst[it] : it; }
+  __device__ __forceinline__ int tile(int it, bool sparse) const { return sparse ? lst[it] : k0 + it; }
 };
 
-template <bool SPARSE>
+template <bool SPARSE, bool PIECE = false>
 __device__ __forceinline__ bool tile_iter(const AttnArgs& a, TileIter& ti) {
   // Dense: XCD x (launch index mod 8) takes a contiguous run of (head, query tile) pairs, so the
-  // workgroups resident on one XCD walk one head's K/V in step and share its L2.  Block-sparse: the
+  // workgroups resident on one XCD walk one head's K/V in step and share its L2.  The last tail_rem tiles
+  // of each run may be split into key-range pieces (a kernel of their own, PIECE).  Block-sparse: the
   // tiles of a head visit different KV subsets and drift apart, so L2 sharing is weak; consecutive
   // launch indices keep the whole chip on about one head at a time instead, whose fragment image is
   // then re-read from the last-level cache rather than HBM (3% faster on the 10 s video layer).
-  int logical = SPARSE ? (int)blockIdx.x : (int)(blockIdx.x & 7) * a.per_xcd + (int)(blockIdx.x >> 3);
-  if (logical >= a.total) return false;
-  if (a.order != 0) logical = a.total - 1 - logical;   // diagnostic reversed order: same work, other timing
+  // The diagnostic reversed order (a.order) permutes the same work within each run.
+  const int nt = (a.nk + BK - 1) / BK;
+  int logical;
+  ti.k0 = 0;
+  ti.slot = 0;
+  ti.ntiles = nt;
+  if constexpr (SPARSE) {
+    logical = (int)blockIdx.x;
+    if (logical >= a.total) return false;
+    if (a.order != 0) logical = a.total - 1 - logical;
+  } else {
+    const int x = (int)(blockIdx.x & 7), x0 = x * a.per_xcd;
+    int j = (int)(blockIdx.x >> 3);
+    if constexpr (!PIECE) {
+      const int valid = min(a.main_per_xcd, a.total - x0);
+      if (j >= valid) return false;
+      if (a.order != 0) j = valid - 1 - j;
+      logical = x0 + j;
+    } else {
+      int piece = j / a.tail_rem, t = j - piece * a.tail_rem;
+      const int valid = min(a.tail_rem, a.total - x0 - a.main_per_xcd);
+      if (piece >= a.tail_pieces || t >= valid) return false;
+      if (a.order != 0) {
+        t = valid - 1 - t;
+        piece = a.tail_pieces - 1 - piece;
+      }
+      logical = x0 + a.main_per_xcd + t;
+      ti.slot = (x * a.tail_rem + t) * a.tail_pieces + piece;
+      ti.k0 = piece * nt / a.tail_pieces;
+      ti.ntiles = (piece + 1) * nt / a.tail_pieces - ti.k0;
+    }
+  }
   ti.head = logical / a.nqt;
   ti.qt = logical - ti.head * a.nqt;
   if constexpr (SPARSE) {
@@ -499,7 +555,6 @@ __device__ __forceinline__ bool tile_iter(const AttnArgs& a, TileIter& ti) {
     ti.lst = a.list + (size_t)logical * a.nb;
     ti.flg = a.list_flags + (size_t)logical * a.nb;
   } else {
-    ti.ntiles = (a.nk + BK - 1) / BK;
     ti.lst = nullptr;
     ti.flg = nullptr;
   }
@@ -700,13 +755,13 @@ __device__ __forceinline__ void tile_body(const uint16_t* T_, int lane, int wave
 }
 
 // Both modes mask keys past the grid (zero K^ and V) in the last, ragged KV tile only.
-template <int D, bool SPARSE, int MODE>
+template <int D, bool SPARSE, int MODE, bool PIECE>
 __device__ __forceinline__ void attn_kernel_body(const AttnArgs& a, uint16_t* sKV) {
   constexpr int QB = Head<D>::QB, BQ = Head<D>::BQ, TILE = Head<D>::TILE;
   constexpr int KS = Head<D>::KS, DB = Head<D>::DB;
   static_assert(BQ % BK == 0, "tile shape");
   TileIter ti;
-  if (!tile_iter<SPARSE>(a, ti)) return;
+  if (!tile_iter<SPARSE, PIECE>(a, ti)) return;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   // A scalar copy of the wave index for the tile copies, whose addresses are then scalar arithmetic.  (Used
   // everywhere, it costs the block-sparse kernel at head dim 96 register spills.)
@@ -768,9 +823,9 @@ __device__ __forceinline__ void attn_kernel_body(const AttnArgs& a, uint16_t* sK
       e_nxt = __builtin_amdgcn_readfirstlane(e_nxt);   // loaded a visit ago
       f_nxt = __builtin_amdgcn_readfirstlane(f_nxt);
     }
-    const int st = it & 1, tile = SPARSE ? e_cur : it;
+    const int st = it & 1, tile = SPARSE ? e_cur : ti.k0 + it;
     if (it + 1 < nt)
-      dma_tile<D>(img + (size_t)(SPARSE ? e_nxt : it + 1) * TILE, wave_s, voff, sKV + (st ^ 1) * TILE);
+      dma_tile<D>(img + (size_t)(SPARSE ? e_nxt : tile + 1) * TILE, wave_s, voff, sKV + (st ^ 1) * TILE);
     const int flags = SPARSE ? f_cur : 0xff;
     int qm = 0;
 #pragma unroll
@@ -797,39 +852,133 @@ __device__ __forceinline__ void attn_kernel_body(const AttnArgs& a, uint16_t* sK
     f_cur = f_nxt;
     f_nxt = f_nn;
   }
-  store_o<D, QB, BQ, SPARSE>(a, ti.head, ti.qt, wave, lane, acc, l);
+  if constexpr (PIECE)
+    store_partial<D>(a, ti.slot, wave, lane, acc, l, negm, mset, MODE == kOnline);
+  else
+    store_o<D, QB, BQ, SPARSE>(a, ti.head, ti.qt, wave, lane, acc, l);
 }
 
-template <int D, bool SPARSE>
+template <int D, bool SPARSE, bool PIECE>
 __global__ void __launch_bounds__(64 * Head<D>::NW) attn_static_kernel(AttnArgs a) {
   __shared__ __attribute__((aligned(16))) uint16_t sKV[2 * Head<D>::TILE];
-  attn_kernel_body<D, SPARSE, kStatic>(a, sKV);
+  attn_kernel_body<D, SPARSE, kStatic, PIECE>(a, sKV);
 }
 
-template <int D, bool SPARSE>
+template <int D, bool SPARSE, bool PIECE>
 __global__ void __launch_bounds__(64 * Head<D>::NW) attn_online_kernel(AttnArgs a) {
   __shared__ __attribute__((aligned(16))) uint16_t sKV[2 * Head<D>::TILE];
-  attn_kernel_body<D, SPARSE, kOnline>(a, sKV);
+  attn_kernel_body<D, SPARSE, kOnline, PIECE>(a, sKV);
+}
+
+// Merge of a split tile's pieces: per lane, the pieces' accumulators and row sums are rescaled to their
+// largest running maximum (the static mode writes 0 for every piece: no rescale) and summed in piece
+// order, then O is normalised and stored as by the unsplit kernels.
+template <int D>
+__global__ void __launch_bounds__(64 * Head<D>::NW) attn_merge_kernel(AttnArgs a) {
+  constexpr int QB = Head<D>::QB, DB = Head<D>::DB, NW = Head<D>::NW, E = kPartialElems<D>;
+  const int x = (int)(blockIdx.x & 7), t = (int)(blockIdx.x >> 3);
+  const int x0 = x * a.per_xcd;
+  if (t >= min(a.tail_rem, a.total - x0 - a.main_per_xcd)) return;
+  const int logical = x0 + a.main_per_xcd + t;
+  const int head = logical / a.nqt, qt = logical - head * a.nqt;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int slot0 = (x * a.tail_rem + t) * a.tail_pieces;
+  f32x16 acc[QB][DB];
+  float l[QB];
+#pragma unroll
+  for (int qb = 0; qb < QB; ++qb) {
+    float mx = -INFINITY;
+    for (int p = 0; p < a.tail_pieces; ++p) {
+      const float* src = a.partial + (((size_t)(slot0 + p) * NW + wave) * QB + qb) * E * 64 + lane;
+      mx = fmaxf(mx, src[(E - 1) * 64]);
+    }
+    l[qb] = 0.f;
+#pragma unroll
+    for (int db = 0; db < DB; ++db) acc[qb][db] = f32x16{};
+    if (mx == -INFINITY) continue;                 // no piece saw a key: O = 0, as unsplit
+    for (int p = 0; p < a.tail_pieces; ++p) {
+      const float* src = a.partial + (((size_t)(slot0 + p) * NW + wave) * QB + qb) * E * 64 + lane;
+      const float m = src[(E - 1) * 64];
+      if (m == -INFINITY) continue;
+      const float f = __builtin_amdgcn_exp2f(m - mx);
+#pragma unroll
+      for (int db = 0; db < DB; ++db)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) acc[qb][db][i] += f * src[(db * 16 + i) * 64];
+      l[qb] += f * src[(E - 2) * 64];
+    }
+  }
+  store_o<D, QB, Head<D>::BQ, false>(a, head, qt, wave, lane, acc, l);
 }
 
 template <int D, bool SPARSE>
 hipError_t launch_attn(const AttnArgs& a, hipStream_t s) {
   hipLaunchKernelGGL(kv_prep_kernel<D>, dim3(a.nb, a.g.heads), dim3(256), 0, s, a);
-  hipError_t e0 = hipGetLastError();
-  if (e0 != hipSuccess) return e0;
-  const int blocks = a.per_xcd * 8;
-  // Both softmax kernels are queued; each checks the weight bound itself and the one that does
-  // not apply returns before touching any data.
-  hipLaunchKernelGGL((attn_static_kernel<D, SPARSE>), dim3(blocks), dim3(64 * Head<D>::NW), 0, s, a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL((attn_online_kernel<D, SPARSE>), dim3(blocks), dim3(64 * Head<D>::NW), 0, s, a);
-  return hipGetLastError();
+  const dim3 block(64 * Head<D>::NW);
+  const int blocks = SPARSE ? a.per_xcd * 8 : a.main_per_xcd * 8;
+  // Both softmax kernels are queued; each checks the weight bound itself and the one that does
+  // not apply returns before touching any data.
+  if (blocks > 0) {
+    hipLaunchKernelGGL((attn_static_kernel<D, SPARSE, false>), dim3(blocks), block, 0, s, a);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+    hipLaunchKernelGGL((attn_online_kernel<D, SPARSE, false>), dim3(blocks), block, 0, s, a);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+  }
+  if constexpr (!SPARSE) {
+    if (a.tail_pieces > 1) {
+      const int pieces = 8 * a.tail_rem * a.tail_pieces;
+      hipLaunchKernelGGL((attn_static_kernel<D, false, true>), dim3(pieces), block, 0, s, a);
+      if ((e = hipGetLastError()) != hipSuccess) return e;
+      hipLaunchKernelGGL((attn_online_kernel<D, false, true>), dim3(pieces), block, 0, s, a);
+      if ((e = hipGetLastError()) != hipSuccess) return e;
+      hipLaunchKernelGGL(attn_merge_kernel<D>, dim3(8 * a.tail_rem), block, 0, s, a);
+      if ((e = hipGetLastError()) != hipSuccess) return e;
+    }
+  }
+  return hipSuccess;
 }
 
 }  // namespace
 
 int attn_query_tile(int head_dim) { return head_dim == 128 ? Head<128>::BQ : Head<96>::BQ; }
+
+size_t tail_partial_bytes(int head_dim) {
+  return head_dim == 128 ? (size_t)Head<128>::NW * Head<128>::QB * kPartialElems<128> * 64 * sizeof(float)
+                         : (size_t)Head<96>::NW * Head<96>::QB * kPartialElems<96> * 64 * sizeof(float);
+}
+
+TailPlan tail_plan(int total, int nk) {
+  constexpr int kCusPerXcd = 32;
+  TailPlan p;
+  p.per_xcd = (total + 7) / 8;
+  p.main_per_xcd = p.per_xcd;
+  p.rem = 0;
+  p.pieces = 1;
+  const int rounds = p.per_xcd / kCusPerXcd, rem = p.per_xcd % kCusPerXcd;
+  const int nt = (nk + BK - 1) / BK;
+  // Small calls are left alone (their whole run is one or a few rounds), and so are key ranges too short
+  // to split.
+  if (rounds < 4 || rem == 0 || nt < 16) return p;
+  // Last-round time, in units of one unsplit tile, with the rem tiles cut into P pieces: ceil(rem P / 32)
+  // rounds of 1/P each.
+  int best = 1;
+  double best_cost = 1.0;
+  for (int P = 2; P <= 4; ++P) {
+    const double cost = (double)((rem * P + kCusPerXcd - 1) / kCusPerXcd) / P;
+    if (cost < best_cost - 1e-9) {
+      best = P;
+      best_cost = cost;
+    }
+  }
+  // worth it only if it saves at least 1% of the call
+  if ((1.0 - best_cost) / (rounds + 1) < 0.01) return p;
+  p.main_per_xcd = p.per_xcd - rem;
+  p.rem = rem;
+  p.pieces = best;
+  return p;
+}
 
 hipError_t launch_attn_dense(const AttnArgs& a, hipStream_t s) {
   return a.head_dim == 128 ? launch_attn<128, false>(a, s) : launch_attn<96, false>(a, s);

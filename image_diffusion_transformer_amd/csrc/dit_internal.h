@@ -62,6 +62,13 @@ struct AttnArgs {
   int total;              // heads * nqt
   int per_xcd;            // ceil(total / 8)
   int order;              // workgroup order: 0 = the tuned one, 1 = reversed (results must not change)
+  // Dense tail split (see TailPlan): the attention kernel takes the first main_per_xcd query tiles of each
+  // XCD's run; the last tail_rem of each run are split along the keys into tail_pieces pieces whose
+  // unnormalised fp32 partials (`partial`) a merge kernel sums.  tail_pieces == 1: no split.
+  int main_per_xcd;
+  int tail_rem;
+  int tail_pieces;
+  float* partial;         // [8 * tail_rem * tail_pieces] x tail_partial_bytes(head_dim)
   // block-sparse iteration lists (null for dense)
   const int* list;        // [heads][nqt][nb]: visited KV tiles, ascending (plain tile indices < nb)
   const unsigned char* list_flags;  // [heads][nqt][nb]: bit s = slot s of the query tile keeps that KV tile
@@ -124,6 +131,20 @@ constexpr size_t tile_image_bytes(int d) { return (size_t)tile_frags(d) * 1024; 
 
 // Query tile of the attention kernel (tokens per workgroup) at head dim d -- a multiple of kBlock.
 int attn_query_tile(int head_dim);
+
+// Dense calls: how the query tiles of the last, partly filled round of workgroups are split.  The tiles run
+// as 8 XCD runs of per_xcd (the launch index mod 8 picks the XCD); each XCD has 32 CUs and one workgroup
+// fits a CU, so a run takes per_xcd / 32 rounds and a last round of rem tiles that leaves 32 - rem CUs idle.
+// When that idle time is worth it, each of those rem tiles is split along the keys into `pieces` parts.
+struct TailPlan {
+  int per_xcd, main_per_xcd, rem, pieces;
+};
+TailPlan tail_plan(int total, int nk);
+// Bytes of one piece's partial result at head dim d.
+size_t tail_partial_bytes(int head_dim);
+inline size_t tail_partial_area(const TailPlan& p, int head_dim) {
+  return p.pieces > 1 ? (size_t)8 * p.rem * p.pieces * tail_partial_bytes(head_dim) : 0;
+}
 
 hipError_t launch_attn_dense(const AttnArgs& a, hipStream_t s);
 hipError_t launch_attn_sparse(const AttnArgs& a, hipStream_t s);

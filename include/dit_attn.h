@@ -65,9 +65,10 @@ typedef enum {
 
 /* Bytes of device workspace that dense, route and block_sparse need for this
  * shape (enough for any of the three; about 2 * N * heads * head_dim * 2 bytes
- * for the K^/V fragment images plus the router's or the block-sparse schedule's
- * share: iteration lists and their slot flags, grouping table and the mask
- * packed to bits).  `sparsity` is the router's (checked to lie in [0, 1)); the
+ * for the K^/V fragment images plus the largest of the router's share, the
+ * block-sparse schedule's (iteration lists and their slot flags, grouping table,
+ * the mask packed to bits) and, for a dense call that splits its last round of
+ * query tiles, the pieces' fp32 partial results).  `sparsity` is the router's (checked to lie in [0, 1)); the
  * size does not depend on it, since block_sparse accepts any mask.
  * Returns 0 if the shape or the sparsity is invalid. */
 size_t dit_attn_workspace_bytes(int T, int H, int W, int heads, int head_dim, int block, float sparsity);
@@ -82,7 +83,14 @@ int dit_attn_keep_count(int nb, float sparsity);
  * K row once and writes K^ (bf16) and V into the workspace as MFMA operand
  * fragments, then the attention kernel: RMSNorm + RoPE of Q on load,
  * S = Q^K^T with bf16 MFMA (fp32 accumulate), softmax in fp32 (base 2),
- * O += P V with bf16 MFMA (P rounded to bf16), O / rowsum rounded to bf16. */
+ * O += P V with bf16 MFMA (P rounded to bf16), O / rowsum rounded to bf16.
+ * Large calls whose query tiles leave the last round of workgroups part-empty
+ * (at least 4 full rounds of 256 tiles, and the split saving at least 1% of
+ * the call) cut each of those last tiles along the keys into 2-4 pieces: the
+ * pieces write unnormalised fp32 partials into the workspace and a third kernel
+ * sums them in piece order and normalises.  Those tiles then differ from an
+ * unsplit evaluation only by the order of the fp32 sums.  The result is the same
+ * bits on every call. */
 dit_status dit_attn_dense(const void* q, const void* k, const void* v,
                           const float* wq, const float* wk,
                           int T, int H, int W, int heads, int head_dim,
@@ -110,7 +118,9 @@ dit_status dit_attn_route(const void* q, const void* k,
  * ([heads][nb][nb] uint8, any 0/1 content, e.g. from dit_attn_route or another
  * source).  Keys of dropped blocks are never loaded; the softmax renormalises
  * over the kept keys.  A query block that keeps no KV block gets O = 0.
- * With an all-ones mask the result equals dit_attn_dense bit for bit. */
+ * With an all-ones mask the result equals dit_attn_dense bit for bit, except on
+ * the query tiles a dense call splits (see dit_attn_dense), where the two agree
+ * up to the order of the fp32 sums. */
 dit_status dit_attn_block_sparse(const void* q, const void* k, const void* v,
                                  const float* wq, const float* wk,
                                  int T, int H, int W, int heads, int head_dim,
@@ -135,8 +145,9 @@ size_t dit_attn_joint_workspace_bytes(int nq, int nk, int heads, int head_dim, i
  *    outside that range are clamped to it (no error is raised on the device).
  *  - RMSNorm, RoPE, softmax and the MFMA path are those of dit_attn_dense; every
  *    query attends to every key.  Writes o [nq][heads][head_dim] bf16.
- *  - With q = k = the grid tokens at their grid positions the result equals
- *    dit_attn_dense bit for bit. */
+ *  - Splits the last round of query tiles as dit_attn_dense does; with q = k =
+ *    the grid tokens at their grid positions the result equals dit_attn_dense
+ *    bit for bit. */
 dit_status dit_attn_joint(const void* q, const void* k, const void* v,
                           const float* wq, const float* wk,
                           const int* q_pos, const int* k_pos,
@@ -157,7 +168,9 @@ dit_status dit_attn_joint(const void* q, const void* k, const void* v,
  *  - Size limit: the RoPE table plus heads * ceil(N / 128) tile images
  *    (48 KiB each at head_dim 96, 64 KiB at 128) must fit the scratch; larger
  *    calls return DIT_ERR_UNSUPPORTED (at head_dim 96 about 1,360 tiles, e.g.
- *    56 heads x 3,072 tokens or 8 heads x 21,760 tokens).
+ *    56 heads x 3,072 tokens or 8 heads x 21,760 tokens).  Calls of this size
+ *    are too small to split their last round of query tiles, so no partials
+ *    are needed.
  *  - The current device must be the stream's device (DIT_ERR_INVALID_ARG).
  *  - All calls on one GPU share its scratch and it keeps the last call's
  *    contents (nothing in it needs to start at zero): calls that overlap in

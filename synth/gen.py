@@ -95,6 +95,14 @@ WORKLOADS = {
                  notes="5 s video grid, 42 heads x 128 (hidden 5376), dense"),
         Workload("v5s128", 31, 48, 84, 42, seed=34, smooth=True, head_dim=128, mode="sparse", sparsity=0.75,
                  notes="same tensors as v5d128, block-sparse at sparsity 0.75"),
+        # head counts whose last round of dense workgroups is partly filled (the kernels split its query tiles
+        # along the keys): 9 x 128 query tiles of 512 at head dim 96, 6 x 200 tiles of 256 at head dim 128
+        Workload("t9", 1, 256, 256, 9, seed=40, smooth=False,
+                 notes="1x256x256 grid, 9 heads: 144 tiles per XCD run, 16 of them in a split last round"),
+        Workload("t9o", 1, 256, 256, 9, seed=40, smooth=False, wq_spike=6.0,
+                 notes="t9's tensors with w_q channel 0 at 6 (running-maximum kernels)"),
+        Workload("t6_128", 1, 200, 256, 6, seed=41, smooth=False, head_dim=128,
+                 notes="1x200x256 grid, 6 heads x 128: 150 tiles per XCD run, 22 of them split"),
         # norm weights 1.75 times as large: the logit bound (59.6 in base 2) is past what exp2 takes without
         # a shift, so the static mode subtracts a constant (bound - 48) from every logit
         Workload("v5w", 31, 48, 84, 56, seed=2, smooth=True, weight_scale=1.75,
