@@ -391,48 +391,61 @@ __device__ __forceinline__ void mask_past_grid(f32x16 (&S)[QB], int key0, int N,
 // Online (running-max) softmax of one sub-block.  S holds the logits less the lane's running max m (the
 // accumulator input of the sub-block's first S MFMA was -m), so p = exp2(S) needs no subtraction; keys >= N get
 // probability 0.  Every p is at most its lane's block sum, so while every sum of the wave stays within
-// kSumLimit no p exceeds it and m needs no update.  The block max is only computed when some sum of the wave is
-// larger, infinite or NaN, or some lane has no max yet (mset false: before its first block with a live key):
-// then m moves up to the block max (to it, for a first block), O and l are rescaled, p is redone with the extra
-// subtraction and -m is written to negm for the next sub-blocks.
+// kSumLimit no p exceeds it and m needs no update.  lim holds the limit a lane's block sum is held to: kSumLimit
+// once the lane has a running max, -1 before its first block with a live key (no sum passes it).  Only when some
+// sum of the wave is past its limit, infinite or NaN is the block max computed: then m moves up to the block max
+// (to it, for a first block), O and l are rescaled, p is redone with the extra subtraction and -m is written to
+// negm for the next sub-blocks.  All query blocks are exponentiated first and checked with one branch.
 // The running max lives only in negm (m = -negm[qb][0]), which gives the block a use besides the MFMA: with
 // the MFMA as its only reader the compiler accumulates in place and copies the block into S every sub-block.
 template <int DB, int QB, int QM = (1 << QB) - 1>
 __device__ __forceinline__ void softmax_online(f32x16 (&S)[QB], bool ragged, int key0, int N, int lane,
-                                               bool (&mset)[QB], f32x16 (&negm)[QB], float (&l)[QB],
+                                               float (&lim)[QB], f32x16 (&negm)[QB], float (&l)[QB],
                                                f32x16 (&acc)[QB][DB], bf16x8 (&P)[QB][2]) {
   if (ragged) mask_past_grid<QB>(S, key0, N, lane);
+  float lb[QB];
+  bool over = false;
 #pragma unroll
   for (int qb = 0; qb < QB; ++qb) {
     if (((QM >> qb) & 1) == 0) continue;
     float p[16];
 #pragma unroll
     for (int i = 0; i < 16; ++i) p[i] = __builtin_amdgcn_exp2f(S[qb][i]);
-    float lb = 0.f;
-    pack_probs(p, lb, P[qb]);
-    if (__builtin_amdgcn_ballot_w64(!mset[qb] || !(lb <= kSumLimit))) {
+    lb[qb] = 0.f;
+    pack_probs(p, lb[qb], P[qb]);
+    over = over || !(lb[qb] <= lim[qb]);
+  }
+  if (__builtin_amdgcn_ballot_w64(over)) {
+#pragma unroll
+    for (int qb = 0; qb < QB; ++qb) {
+      if (((QM >> qb) & 1) == 0) continue;
+      if (!__builtin_amdgcn_ballot_w64(!(lb[qb] <= lim[qb]))) continue;
+      const bool has_max = lim[qb] >= 0.f;
       float mx = S[qb][0];
 #pragma unroll
       for (int i = 1; i < 16; ++i) mx = fmaxf(mx, S[qb][i]);
       mx = pair_max(mx);
       // raise of m: up to the block max (to it, for a lane without a max yet); none for a block of masked keys
       const bool live = mx > -INFINITY;
-      const float d = live ? (mset[qb] ? fmaxf(mx, 0.f) : mx) : 0.f;
+      const float d = live ? (has_max ? fmaxf(mx, 0.f) : mx) : 0.f;
       const float alpha = __builtin_amdgcn_exp2f(-d);
       l[qb] *= alpha;
 #pragma unroll
       for (int db = 0; db < DB; ++db) acc[qb][db] *= alpha;
       const float mnew = d - negm[qb][0];
-      mset[qb] = mset[qb] || live;
+      lim[qb] = (has_max || live) ? kSumLimit : -1.f;
+      float p[16];
 #pragma unroll
       for (int i = 0; i < 16; ++i) p[i] = __builtin_amdgcn_exp2f(S[qb][i] - d);
-      lb = 0.f;
-      pack_probs(p, lb, P[qb]);
+      lb[qb] = 0.f;
+      pack_probs(p, lb[qb], P[qb]);
 #pragma unroll
       for (int i = 0; i < 16; ++i) negm[qb][i] = -mnew;
     }
-    l[qb] += lb;
   }
+#pragma unroll
+  for (int qb = 0; qb < QB; ++qb)
+    if ((QM >> qb) & 1) l[qb] += lb[qb];
 }
 
 // Static-shift softmax of one sub-block: p = exp2(S), S already holding the logits less the constant shift.
@@ -484,7 +497,7 @@ template <int D>
 __device__ __forceinline__ void store_partial(const AttnArgs& a, int slot, int wave, int lane,
                                               const f32x16 (&acc)[Head<D>::QB][Head<D>::DB],
                                               const float (&l)[Head<D>::QB], const f32x16 (&negm)[Head<D>::QB],
-                                              const bool (&mset)[Head<D>::QB], bool online) {
+                                              const float (&lim)[Head<D>::QB], bool online) {
   constexpr int QB = Head<D>::QB, DB = Head<D>::DB, NW = Head<D>::NW, E = kPartialElems<D>;
 #pragma unroll
   for (int qb = 0; qb < QB; ++qb) {
@@ -494,7 +507,7 @@ __device__ __forceinline__ void store_partial(const AttnArgs& a, int slot, int w
 #pragma unroll
       for (int i = 0; i < 16; ++i) dst[(db * 16 + i) * 64] = acc[qb][db][i];
     dst[(E - 2) * 64] = l[qb];
-    dst[(E - 1) * 64] = online ? (mset[qb] ? -negm[qb][0] : -INFINITY) : 0.f;
+    dst[(E - 1) * 64] = online ? (lim[qb] >= 0.f ? -negm[qb][0] : -INFINITY) : 0.f;
   }
 }
 
@@ -705,7 +718,7 @@ __device__ __forceinline__ void raise_younger_wave(int kb, int wave) {
 template <int D, int QB, int QM, int MODE>
 __device__ __forceinline__ void tile_body(const uint16_t* T_, int lane, int wave, bool balance,
                                           const bf16x8 (&qf)[QB][Head<D>::KS],
-                                          f32x16 (&acc)[QB][Head<D>::DB], bool (&mset)[QB], f32x16 (&negm)[QB],
+                                          f32x16 (&acc)[QB][Head<D>::DB], float (&lim)[QB], f32x16 (&negm)[QB],
                                           float (&l)[QB], const f32x16& negc, bool ragged, int key0, int N) {
   constexpr int KS = Head<D>::KS;
   if constexpr (MODE == kStatic) {
@@ -748,7 +761,7 @@ __device__ __forceinline__ void tile_body(const uint16_t* T_, int lane, int wave
       f32x16 S[QB];
       qk_block<D, QB, QM>(T_, kb, lane, qf, negm, S);
       bf16x8 P[QB][2];
-      softmax_online<Head<D>::DB, QB, QM>(S, ragged, key0 + kb * 32, N, lane, mset, negm, l, acc, P);
+      softmax_online<Head<D>::DB, QB, QM>(S, ragged, key0 + kb * 32, N, lane, lim, negm, l, acc, P);
       pv_block<D, QB, QM>(T_, kb, lane, P, acc);
     }
   }
@@ -790,11 +803,11 @@ __device__ __forceinline__ void attn_kernel_body(const AttnArgs& a, uint16_t* sK
   // Online mode: -m, the running max of the lane's query (0 and not yet set before its first block with a
   // live key), in every element of negm, the accumulator input of each sub-block's first S MFMA.
   float l[QB];
-  bool mset[QB];
+  float lim[QB];
   f32x16 negm[QB];
 #pragma unroll
   for (int qb = 0; qb < QB; ++qb) {
-    mset[qb] = false;
+    lim[qb] = -1.f;
     negm[qb] = f32x16{};
     l[qb] = 0.f;
 #pragma unroll
@@ -834,15 +847,15 @@ __device__ __forceinline__ void attn_kernel_body(const AttnArgs& a, uint16_t* sK
     const bool ragged = (tile + 1) * BK > N;
     if constexpr (SPARSE && QB == 2) {
       if (qm == 3)
-        tile_body<D, QB, 3, MODE>(T_, lane, wave, false, qf, acc, mset, negm, l, negc, ragged, tile * BK, N);
+        tile_body<D, QB, 3, MODE>(T_, lane, wave, false, qf, acc, lim, negm, l, negc, ragged, tile * BK, N);
       else if (qm == 1)
-        tile_body<D, QB, 1, MODE>(T_, lane, wave, false, qf, acc, mset, negm, l, negc, ragged, tile * BK, N);
+        tile_body<D, QB, 1, MODE>(T_, lane, wave, false, qf, acc, lim, negm, l, negc, ragged, tile * BK, N);
       else if (qm == 2)
-        tile_body<D, QB, 2, MODE>(T_, lane, wave, false, qf, acc, mset, negm, l, negc, ragged, tile * BK, N);
+        tile_body<D, QB, 2, MODE>(T_, lane, wave, false, qf, acc, lim, negm, l, negc, ragged, tile * BK, N);
     } else if constexpr (SPARSE) {
-      if (qm != 0) tile_body<D, QB, (1 << QB) - 1, MODE>(T_, lane, wave, false, qf, acc, mset, negm, l, negc, ragged, tile * BK, N);
+      if (qm != 0) tile_body<D, QB, (1 << QB) - 1, MODE>(T_, lane, wave, false, qf, acc, lim, negm, l, negc, ragged, tile * BK, N);
     } else {
-      tile_body<D, QB, (1 << QB) - 1, MODE>(T_, lane, wave, true, qf, acc, mset, negm, l, negc, ragged, tile * BK,
+      tile_body<D, QB, (1 << QB) - 1, MODE>(T_, lane, wave, true, qf, acc, lim, negm, l, negc, ragged, tile * BK,
                                             N);
     }
     tile_barrier();
@@ -853,7 +866,7 @@ __device__ __forceinline__ void attn_kernel_body(const AttnArgs& a, uint16_t* sK
     f_nxt = f_nn;
   }
   if constexpr (PIECE)
-    store_partial<D>(a, ti.slot, wave, lane, acc, l, negm, mset, MODE == kOnline);
+    store_partial<D>(a, ti.slot, wave, lane, acc, l, negm, lim, MODE == kOnline);
   else
     store_o<D, QB, BQ, SPARSE>(a, ti.head, ti.qt, wave, lane, acc, l);
 }
