@@ -256,6 +256,17 @@ def test_host_allocation_failure_returns_status_not_exception():
     assert "host memory" in msg
 
 
+def test_workspace_covers_the_tail_split_partials(lib):
+    # 7 heads of the 5 s grid: 1715 query tiles, 215 per XCD run = 6 rounds of 32 and 23 more, which the dense
+    # call cuts into 4 key-range pieces each: 8 x 23 x 4 fp32 partials of 8 waves x 2 blocks x (3 x 16 + 2) x 64
+    nb = 977
+    partials = 8 * 23 * 4 * (8 * 2 * 50 * 64 * 4)
+    n = dit.dit_attn_workspace_bytes(31, 48, 84, 7)
+    assert n >= 7 * nb * 48 * 1024 + partials
+    # the same tiles as one joint call (queries = keys = the grid tokens) split the same way
+    assert dit.dit_attn_joint_workspace_bytes(124992, 124992, 7, 96, 84) >= 7 * nb * 48 * 1024 + partials
+
+
 def test_joint_workspace_bytes(lib):
     n = dit.dit_attn_joint_workspace_bytes(65536, 197120, 56, 96, 515)
     assert n >= 56 * 1540 * 48 * 1024 + 515 * 32 * 4          # fragment images of 1540 key tiles + table
