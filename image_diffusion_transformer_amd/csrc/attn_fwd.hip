@@ -755,9 +755,11 @@ __device__ __forceinline__ void tile_body(const uint16_t* T_, int lane, int wave
     kp[1] = *(const bf16x8*)(T_ + 1 * kFrag + lane * 8);
     auto sub_block = [&](int kb) {
       if (balance) raise_younger_wave(kb, wave);
-      if (cj.on) dma_part<D>(cj, kb);
+      // copy part: before the S MFMAs at head dim 96, after them at 128 (each measured the faster there)
+      if (D == 96 && cj.on) dma_part<D>(cj, kb);
       f32x16 S[QB];
       qk_block_pre<D, QB, QM>(T_, kb, lane, qf, kp, negc, S);
+      if (D == 128 && cj.on) dma_part<D>(cj, kb);
       const int nk = kb + 1 < BK / 32 ? kb + 1 : kb;   // the last sub-block re-reads its own (unused)
       kp[0] = *(const bf16x8*)(T_ + (nk * KS + 0) * kFrag + lane * 8);
       kp[1] = *(const bf16x8*)(T_ + (nk * KS + 1) * kFrag + lane * 8);
