@@ -79,16 +79,16 @@ size_t dit_attn_workspace_bytes(int T, int H, int W, int heads, int head_dim, in
 int dit_attn_keep_count(int nb, float sparsity);
 
 /* Dense attention.  Writes o [N][heads][head_dim] bf16.
- * Two kernels on `hip_stream`: a prepass that RMS-normalises and rotates every
+ * Kernels on `hip_stream`: a prepass that RMS-normalises and rotates every
  * K row once and writes K^ (bf16) and V into the workspace as MFMA operand
  * fragments, then the attention kernel: RMSNorm + RoPE of Q on load,
  * S = Q^K^T with bf16 MFMA (fp32 accumulate), softmax in fp32 (base 2),
  * O += P V with bf16 MFMA (P rounded to bf16), O / rowsum rounded to bf16.
  * Large calls whose query tiles leave the last round of workgroups part-empty
- * (at least 4 full rounds of 256 tiles, and the split saving at least 1% of
- * the call) cut each of those last tiles along the keys into 2-4 pieces: the
- * pieces write unnormalised fp32 partials into the workspace and a third kernel
- * sums them in piece order and normalises.  Those tiles then differ from an
+ * (at least 4 full rounds of 256 tiles, at least 16 key tiles of 128, and the
+ * split saving at least 1% of the call) cut each of those last tiles along the
+ * keys into 2-4 pieces: the pieces write unnormalised fp32 partials into the
+ * workspace and a third kernel sums them in piece order and normalises.  Those tiles then differ from an
  * unsplit evaluation only by the order of the fp32 sums.  The result is the same
  * bits on every call. */
 dit_status dit_attn_dense(const void* q, const void* k, const void* v,
