@@ -4,7 +4,8 @@ The query tiles run as 8 XCD runs of ceil(tiles / 8) each, 32 CUs per XCD and on
 run has at least 4 full rounds and a last round of rem < 32 tiles, and cutting each of those tiles into P
 (2..4) key-range pieces saves at least 1% of the call, the pieces write fp32 partial results that a merge
 kernel sums.  The rule is restated here to find the split tiles, which are then checked:
-  * against the fp64 oracle (static and running-maximum softmax, head dim 96 and 128);
+  * against the fp64 oracle (static and running-maximum softmax, head dim 96 and 128, and the full-size
+    7-head share of the 5 s video layer, the sharded case the split is for);
   * against the block-sparse call with an all-ones mask, which never splits: every other tile bitwise equal,
     split tiles within the rounding of a different summation order;
   * for determinism: a repeated call and the reversed workgroup order give the same bits;
@@ -72,7 +73,7 @@ def rows_of(wl, qt):
     return np.unique(np.concatenate([np.arange(lo, min(hi, lo + 128)), np.arange(max(lo, hi - 128), hi)]))
 
 
-@pytest.mark.parametrize("name,pieces", [("t9", 2), ("t9o", 2), ("t6_128", 4)])
+@pytest.mark.parametrize("name,pieces", [("t9", 2), ("t9o", 2), ("t6_128", 4), ("v5h7", 4)])
 def test_split_tiles_match_the_oracle(name, pieces):
     x = make_inputs(name)
     wl = x.workload
