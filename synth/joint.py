@@ -66,6 +66,9 @@ JOINT_WORKLOADS = {
                       notes="j_small's sequence at head dim 128"),
         JointWorkload("j_edit2", 512, ((256, 256), (256, 256)), (1, 256, 256), 56, seed=23,
                       notes="image edit with 2 reference images: 197,120 keys, 65,536 target queries"),
+        JointWorkload("j_ref9", 512, ((128, 128),), (1, 256, 256), 9, seed=25,
+                      notes="one reference image, 9 heads: 82,432 keys, 65,536 target queries; 144 query tiles "
+                            "per XCD run, so the dense tail split applies"),
     ]
 }
 

@@ -19,7 +19,7 @@ import torch
 
 import image_diffusion_transformer_amd as dit
 from oracle import attention as A
-from synth import make_inputs
+from synth import make_inputs, make_joint_inputs
 
 pytestmark = pytest.mark.gpu
 DEV = torch.device("cuda:0")
@@ -146,3 +146,29 @@ def test_joint_at_grid_positions_splits_alike():
     b = dit.dit_attn_joint(q, k, v, wq, wk, pos, pos, int(pos.max()) + 1, wl.theta, wl.eps)
     torch.cuda.synchronize()
     assert torch.equal(a, b)
+
+
+def test_joint_with_more_keys_than_queries_splits_against_the_oracle():
+    """Joint call, 65,536 target queries against 82,432 keys (text, one reference image, target), 9 heads:
+    its split tiles cut the longer key range."""
+    x = make_joint_inputs("j_ref9")
+    wl = x.workload
+    nqt = -(-wl.Nq // 512)
+    total = wl.heads * nqt
+    per, main, rem, pieces = plan(total, wl.Nkv)
+    assert pieces == 2 and rem > 0
+    t16 = lambda b: torch.from_numpy(b.bits.view(np.int16)).to(DEV).view(torch.bfloat16)
+    tpos = lambda p: torch.from_numpy(np.ascontiguousarray(p, dtype=np.int32)).to(DEV)
+    o = dit.dit_attn_joint(t16(x.q), t16(x.k), t16(x.v), torch.from_numpy(x.wq).to(DEV),
+                           torch.from_numpy(x.wk).to(DEV), tpos(x.q_pos), tpos(x.k_pos), x.max_pos, wl.theta, wl.eps)
+    torch.cuda.synchronize()
+    split = [divmod(x0 * per + main + t, nqt) for x0 in range(8) for t in range(rem) if x0 * per + main + t < total]
+    for head, qt in [split[0], split[-1], (0, 0)]:
+        rows = np.concatenate([np.arange(qt * 512, qt * 512 + 128), np.arange(qt * 512 + 384, qt * 512 + 512)])
+        ref = A.attention_joint(x.q, x.k, x.v, x.wq, x.wk, x.q_pos, x.k_pos, wl.theta, wl.eps, heads=[head],
+                                rows=rows)
+        got = o[torch.from_numpy(rows).to(DEV), head].float().cpu().numpy().astype(np.float64)
+        err = np.abs(got - ref[:, 0])
+        rel = float(np.linalg.norm(err) / np.linalg.norm(ref))
+        print(f"j_ref9 head {head} tile {qt}: max_abs={err.max():.3e} rel_l2={rel:.3e}", flush=True)
+        assert np.all(np.isfinite(got)) and err.max() <= MAX_ABS and rel <= REL_L2
