@@ -237,7 +237,7 @@ def bench_joint(args, torch, dit):
         "frac_of_bf16_peak": round(tflops / PEAK_BF16_TFLOPS, 4),
         "roofline": {"bound": "mfma", "achieved": round(flops / (ms_call * 1e-3) / 1e12, 2), "peak": PEAK_BF16_TFLOPS,
                      "unit": "TFLOP/s", "frac": round(flops / (ms_call * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4),
-                     "traffic": None, "kernel": f"attn_static_kernel<{wl.head_dim}, false>", "kernel_ms": round(ms_call, 3),
+                     "traffic": None, "kernel": f"attn_static_kernel<{wl.head_dim}, false, false>", "kernel_ms": round(ms_call, 3),
                      "timed": "whole call: K^/V fragment prepass + attention kernels", "flops_per_launch": flops},
         "call_ms": timing_summary(call_ms),
         "sclk": clk.summary(),
@@ -504,7 +504,7 @@ def main():
         "frac_of_bf16_peak": round(tflops / PEAK_BF16_TFLOPS, 4),
         "roofline": {"bound": "mfma", "achieved": round(attn_tflops, 2), "peak": PEAK_BF16_TFLOPS,
                      "unit": "TFLOP/s", "frac": round(attn_tflops / PEAK_BF16_TFLOPS, 4), "traffic": traffic,
-                     "kernel": f"attn_{softmax_mode(x.wq, x.wk, d)}_kernel<{d}, " + ("true>" if sparse else "false>"),
+                     "kernel": f"attn_{softmax_mode(x.wq, x.wk, d)}_kernel<{d}, " + ("true, false>" if sparse else "false, false>"),
                      "timed": "whole call: K^/V fragment prepass + attention kernels",
                      "kernel_ms": round(ms_attn, 3), "flops_per_launch": flops},
         # per-step event timings of the attention call (and of the router call for sparse workloads)
