@@ -25,8 +25,13 @@
 //  * KV tiles are double-buffered in LDS: the next tile's fragment image is in
 //    flight (global->LDS, no registers, issued as inline assembly so that the
 //    fragment reads get graded LDS waits) while the current one is consumed.
-//    Block-sparse tiles take their KV tile and slot flags from per-tile lists
-//    whose entries are loaded two visits ahead.
+//    Dense calls issue that copy in parts, one per 32-key sub-block, so its LDS
+//    writes interleave with the fragment reads.  Block-sparse tiles take their KV
+//    tile and slot flags from per-tile lists whose entries are loaded two visits
+//    ahead.
+//  * Dense calls whose last round of workgroups would leave CUs idle split those
+//    query tiles along the keys into pieces with fp32 partial results, which a
+//    merge kernel sums (tail_plan).
 //  * S^T = K^ Q^T with v_mfma_f32_32x32x16_bf16 (keys on rows, queries on columns):
 //    each lane holds one query column, so the softmax row statistics need only
 //    in-lane reductions plus one permlane32 swap, and the S^T accumulator is
@@ -36,9 +41,10 @@
 //  * Static-shift softmax when the QK-RMSNorm logit bound B allows it (B <= 80 in
 //    base 2: p = exp2(S - c), c = max(0, B - 48) taken as the first S MFMA's
 //    accumulator input, no running max); otherwise an online softmax in base 2 whose running max
-//    only moves (and O, l are rescaled) when a lane's block sum of p passes 2^8,
-//    so every p stays <= 2^8 and the block max is computed only then; the final
-//    O / l is exact for any stale max.
+//    m enters the same way (-m as the accumulator input) and only moves (and O, l
+//    are rescaled) when a lane's block sum of p passes 2^8, so every p stays
+//    <= 2^8 and the block max is computed only then; the final O / l is exact
+//    for any stale max.
 //  * Row sums accumulate the bf16-rounded probabilities (v_dot2_f32_bf16), the
 //    same values the PV product uses.
 #include "dit_internal.h"
