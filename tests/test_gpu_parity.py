@@ -148,6 +148,25 @@ def test_dense_running_max_rescale(weights):
     check_close(got, ref, f"dense late max ({weights} weights)")
 
 
+@pytest.mark.parametrize("bad", [float("nan"), float("inf")])
+def test_non_finite_norm_weight_gives_non_finite_rows_not_garbage(bad):
+    """A NaN or infinite norm weight has no logit bound, so the running-maximum kernel takes the call (the static
+    one returns at once).  Every q^ then carries a non-finite channel, every logit is NaN and so is every O
+    element in the fp64 oracle too: the call completes and writes NaN everywhere, dense and block-sparse."""
+    x = make_inputs("s3")
+    wl = x.workload
+    q, k, v, wq, wk = upload(x)
+    wq[5] = bad
+    ref = A.attention(x.q, x.k, x.v, np.where(np.arange(96) == 5, np.float32(bad), x.wq), x.wk, wl.T, wl.H, wl.W,
+                      wl.theta, wl.eps, heads=[0], rows=np.arange(64))
+    assert np.all(np.isnan(ref))
+    o = dit.dit_attn_dense(q, k, v, wq, wk, grid(wl))
+    ones = torch.ones((wl.heads, wl.nb, wl.nb), dtype=torch.uint8, device=DEV)
+    os_ = dit.dit_attn_block_sparse(q, k, v, wq, wk, grid(wl), ones)
+    torch.cuda.synchronize()
+    assert bool(torch.isnan(o).all()) and bool(torch.isnan(os_).all())
+
+
 def test_dense_deterministic():
     x = make_inputs("s4")
     a = run_dense(x)
