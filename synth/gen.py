@@ -103,6 +103,8 @@ WORKLOADS = {
                  notes="t9's tensors with w_q channel 0 at 6 (running-maximum kernels)"),
         Workload("t6_128", 1, 200, 256, 6, seed=41, smooth=False, head_dim=128,
                  notes="1x200x256 grid, 6 heads x 128: 150 tiles per XCD run, 22 of them split"),
+        Workload("t6_128o", 1, 200, 256, 6, seed=41, smooth=False, head_dim=128, wq_spike=6.0,
+                 notes="t6_128's tensors with w_q channel 0 at 6 (running-maximum kernels)"),
         # norm weights 1.75 times as large: the logit bound (59.6 in base 2) is past what exp2 takes without
         # a shift, so the static mode subtracts a constant (bound - 48) from every logit
         Workload("v5w", 31, 48, 84, 56, seed=2, smooth=True, weight_scale=1.75,

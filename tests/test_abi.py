@@ -267,6 +267,27 @@ def test_workspace_covers_the_tail_split_partials(lib):
     assert dit.dit_attn_joint_workspace_bytes(124992, 124992, 7, 96, 84) >= 7 * nb * 48 * 1024 + partials
 
 
+def test_calls_within_the_noalloc_scratch_never_split_their_last_round(lib):
+    # The dense tail split (restated: 8 XCD runs of ceil(tiles / 8), 32 CUs each; at least 4 full rounds, at
+    # least 16 key tiles, 2-4 pieces, at least 1% saved) needs many more query tiles than the 64 MiB static
+    # scratch of dit_attn_dense_noalloc can hold fragment images for, so that entry point needs no partials.
+    import math
+    cap = dit.NOALLOC_SCRATCH_BYTES
+
+    def splits(total, nt):
+        per = (total + 7) // 8
+        rounds, rem = divmod(per, 32)
+        if rounds < 4 or rem == 0 or nt < 16:
+            return False
+        return min(math.ceil(rem * p / 32) / p for p in (2, 3, 4)) <= 1 - 0.01 * (rounds + 1)
+
+    for d, bq, tile in ((96, 512, 48 * 1024), (128, 256, 64 * 1024)):
+        for nb in range(16, 1400):
+            heads_max = cap // (nb * tile)
+            for heads in range(1, heads_max + 1):
+                assert not splits(heads * -(-nb * 128 // bq), nb), (d, nb, heads)
+
+
 def test_joint_workspace_bytes(lib):
     n = dit.dit_attn_joint_workspace_bytes(65536, 197120, 56, 96, 515)
     assert n >= 56 * 1540 * 48 * 1024 + 515 * 32 * 4          # fragment images of 1540 key tiles + table

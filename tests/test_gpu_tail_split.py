@@ -73,7 +73,7 @@ def rows_of(wl, qt):
     return np.unique(np.concatenate([np.arange(lo, min(hi, lo + 128)), np.arange(max(lo, hi - 128), hi)]))
 
 
-@pytest.mark.parametrize("name,pieces", [("t9", 2), ("t9o", 2), ("t6_128", 4), ("v5h7", 4)])
+@pytest.mark.parametrize("name,pieces", [("t9", 2), ("t9o", 2), ("t6_128", 4), ("t6_128o", 4), ("v5h7", 4)])
 def test_split_tiles_match_the_oracle(name, pieces):
     x = make_inputs(name)
     wl = x.workload
@@ -120,7 +120,7 @@ def test_split_against_the_unsplit_block_sparse_path(name):
     assert float(diff.max()) <= 2e-3
 
 
-@pytest.mark.parametrize("name", ["t9", "t9o"])
+@pytest.mark.parametrize("name", ["t9", "t9o", "t6_128", "t6_128o"])
 def test_split_is_deterministic_in_either_workgroup_order(name):
     x = make_inputs(name)
     wl = x.workload
