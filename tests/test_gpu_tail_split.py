@@ -19,7 +19,7 @@ import torch
 
 import image_diffusion_transformer_amd as dit
 from oracle import attention as A
-from synth import make_inputs, make_joint_inputs
+from synth import custom_workload, make_inputs, make_joint_inputs
 
 pytestmark = pytest.mark.gpu
 DEV = torch.device("cuda:0")
@@ -171,4 +171,41 @@ def test_joint_with_more_keys_than_queries_splits_against_the_oracle():
         err = np.abs(got - ref[:, 0])
         rel = float(np.linalg.norm(err) / np.linalg.norm(ref))
         print(f"j_ref9 head {head} tile {qt}: max_abs={err.max():.3e} rel_l2={rel:.3e}", flush=True)
+        assert np.all(np.isfinite(got)) and err.max() <= MAX_ABS and rel <= REL_L2
+
+
+# Seeded shapes in the split regime with ragged last blocks, both head dims, 2-4 pieces; the last two with one
+# large w_q channel, which sends them to the running-maximum kernels.
+SHAPES = [(6, 84, 70, 12, 128, 0.0), (5, 79, 59, 16, 128, 0.0), (5, 92, 76, 23, 96, 0.0),
+          (6, 79, 85, 14, 128, 6.0), (5, 92, 76, 23, 96, 6.0)]
+
+
+@pytest.mark.parametrize("T,H,W,heads,d,spike", SHAPES)
+def test_split_on_seeded_ragged_shapes(T, H, W, heads, d, spike):
+    wl = custom_workload(T, H, W, heads, seed=50 + T + H + W + heads, smooth=True, head_dim=d, wq_spike=spike)
+    print(f"case {wl.name} d={d} spike={spike}", flush=True)
+    x = make_inputs(wl)
+    tiles, p = split_tiles(wl)
+    assert p > 1 and tiles
+    q, k, v, wq, wk = upload(x)
+    g = (wl.T, wl.H, wl.W)
+    o = dit.dit_attn_dense(q, k, v, wq, wk, g, wl.theta, wl.eps)
+    try:
+        dit.dit_attn_set_launch_order(1)
+        o_rev = dit.dit_attn_dense(q, k, v, wq, wk, g, wl.theta, wl.eps)
+    finally:
+        dit.dit_attn_set_launch_order(0)
+    torch.cuda.synchronize()
+    assert torch.equal(o, o_rev)
+    bq = query_tile(d)
+    nqt = -(-wl.N // bq)
+    last = next(((h, t) for h, t in tiles if t == nqt - 1), (wl.heads - 1, nqt - 1))
+    for head, qt in [tiles[0], tiles[-1], last]:
+        rows = rows_of(wl, qt)
+        ref = A.attention(x.q, x.k, x.v, x.wq, x.wk, wl.T, wl.H, wl.W, wl.theta, wl.eps, heads=[head], rows=rows)
+        got = o[torch.from_numpy(rows).to(DEV), head].float().cpu().numpy().astype(np.float64)
+        err = np.abs(got - ref[:, 0])
+        rel = float(np.linalg.norm(err) / np.linalg.norm(ref))
+        print(f"  head {head} tile {qt} ({'split' if (head, qt) in set(tiles) else 'whole'}): "
+              f"max_abs={err.max():.3e} rel_l2={rel:.3e}", flush=True)
         assert np.all(np.isfinite(got)) and err.max() <= MAX_ABS and rel <= REL_L2
